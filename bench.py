@@ -1,0 +1,288 @@
+"""Benchmark of the segment-attention hot path on one MI355X.
+
+One step = one pass of the hot path over one segment of the 480x832 workload
+(16 heads x 128 dims, 30 latent frames x 390 tokens = 11,700 video queries,
+768-token description head + 4 action tails of 128 tokens, no history):
+    hn_attn_mask_build (tile plan) -> hn_seg_attn_fwd -> hn_kv_quant_append.
+Inputs are seeded synthetic bf16 N(0,1) tensors already resident in HBM.
+
+value = effective attention FLOPs of the step / step time, where effective
+FLOPs count only unmasked (query, key) pairs: 4 * D per pair per head
+(Q K^T and P V multiply-adds).  The roofline object reports the attention
+kernel alone (HIP events around each launch on its stream) against the bf16
+dense MFMA peak; the append object reports the quantize/append kernel's
+bytes (776 per (token, head): 512 read, 256 INT8 + 8 scale bytes written)
+against 8 TB/s, with rotating buffers so the bytes come from HBM.
+cpu_baseline times the fp64 CPU oracle on a sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective attention TFLOP/s (unmasked pairs) + % bf16 MFMA peak; KV append GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+APPEND_BYTES_PER_ROW = 2 * 128 * 2 + 2 * 128 + 2 * 4   # 776
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", help="c2 (default), c3, c4 or c5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=11700, help="query rows the oracle computes")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--traffic", default=None,
+                    help="JSON {fetch_kib, write_kib, scale} per attention launch from counters")
+    return ap.parse_args()
+
+
+def visible_pairs(w, csr=None):
+    """Unmasked (query, key) pairs per head, from the layout (no oracle)."""
+    S = w.query_segment
+    cur = w.current
+    P = cur.tokens_per_frame
+    g0 = sum(s.frames for s in w.segments[:S])
+    kept = g0 if w.window is None else min(g0, w.window)
+    hist_heads = sum(s.head_len for s in w.segments[:S])
+    if csr is None:
+        tot = 0
+        for f in range(cur.frames):
+            n = hist_heads + kept * P + cur.head_len + cur.video_len
+            n += sum(a for a, f0, f1 in zip(cur.action_len, cur.action_f0, cur.action_f1) if f0 <= f < f1)
+            tot += n * P
+        return tot
+    # block-sparse: text + kept video tiles
+    n_hist_tiles = -(-kept * P // 128)
+    def tile_len(c):
+        if c < n_hist_tiles:
+            return min(128, kept * P - c * 128)
+        c -= n_hist_tiles
+        return min(128, cur.video_len - c * 128)
+    tot = 0
+    for r in range(cur.video_len):
+        f = r // P
+        t = r // 128
+        n = hist_heads + cur.head_len
+        n += sum(a for a, f0, f1 in zip(cur.action_len, cur.action_f0, cur.action_f1) if f0 <= f < f1)
+        cols = csr["col"][csr["row_ptr"][t]:csr["row_ptr"][t + 1]]
+        n += sum(tile_len(int(c)) for c in cols)
+        tot += n
+    return tot
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the method shards by attention head with no exchange inside the path)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if not os.path.exists(os.path.join(ROOT, "masked_attention_hn_amd", "libhn.so")):
+        import __graft_entry__
+        __graft_entry__.build()
+    import masked_attention_hn_amd as hn
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n, "launches": 3}))
+        return
+
+    w = W.config(args.workload)
+    data = W.generate(w)
+    to_dev = lambda x: torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def lay(i, s):
+        return hn.SegLayout(i, s.frames, s.tokens_per_frame, s.head_len, s.action_len,
+                            s.action_f0, s.action_f1)
+
+    cache = hn.KVCache(w.heads, w.current.tokens_per_frame, w.ring_frames, w.head_cap)
+    for s in range(w.query_segment):
+        x = data["segments"][s]
+        hn.hn_kv_quant_append(cache, lay(s, w.segments[s]), to_dev(x["k_txt"]), to_dev(x["v_txt"]),
+                              to_dev(x["k_vid"]), to_dev(x["v_vid"]))
+    S = w.query_segment
+    seg = lay(S, w.current)
+    x = data["segments"][S]
+    k_txt, v_txt, k_vid, v_vid = (to_dev(x[n]) for n in ("k_txt", "v_txt", "k_vid", "v_vid"))
+    q = to_dev(data["q_vid"])
+    o = torch.empty_like(q)
+    sparse = None
+    csr = None
+    if w.sparse_keep is not None:
+        csr = data["csr"]
+        sparse = hn.BlockSparse(torch.from_numpy(csr["row_ptr"]), torch.from_numpy(csr["col"]),
+                                csr["n_qtiles"])
+    ws = torch.empty(hn.hn_attn_workspace_size(cache, seg, sparse), dtype=torch.uint8, device=dev)
+    plan_c = hn.hn_tile_plan()
+    plan = hn.Plan(ws, plan_c)
+    saved = (cache.c.frames_seen, cache.c.head_tokens, cache.c.segments)
+    pairs = visible_pairs(w, csr)
+    flops = 4.0 * 128 * pairs * w.heads
+    surv_frames = min(w.current.frames, w.ring_frames)
+    append_rows = (w.current.head_len + surv_frames * w.current.tokens_per_frame) * w.heads
+    append_bytes = append_rows * APPEND_BYTES_PER_ROW
+
+    ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+
+    def step(i=None, timed=False):
+        cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
+        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c)
+        if timed:
+            ev_a0[i].record(stream)
+        hn.hn_seg_attn_fwd(cache, seg, plan, q, k_txt, v_txt, k_vid, v_vid, o)
+        if timed:
+            ev_a1[i].record(stream)
+        hn.hn_kv_quant_append(cache, seg, k_txt, v_txt, k_vid, v_vid)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timed=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    attn_ms = [a.elapsed_time(b) for a, b in zip(ev_a0, ev_a1)]
+    attn_avg = sum(attn_ms) / len(attn_ms)
+    achieved = flops / (attn_avg * 1e-3) / 1e12
+    value = flops / (ms_step * 1e-3) / 1e12
+    if plan_c.visible_pairs >= 0:
+        assert plan_c.visible_pairs == pairs, (plan_c.visible_pairs, pairs)
+
+    # quantize/append alone, rotating input and ring buffers (> 256 MB MALL)
+    n_sets = max(3, math.ceil(600e6 / max(1, append_bytes)))
+    sets = []
+    for r in range(n_sets):
+        c = hn.KVCache(w.heads, w.current.tokens_per_frame, w.ring_frames, max(1, w.current.head_len))
+        kv = [t.clone() for t in (k_txt, v_txt, k_vid, v_vid)]
+        sets.append((c, kv))
+    seg0 = lay(0, w.current)
+    for c, kv in sets:
+        hn.hn_kv_quant_append(c, seg0, *kv)
+        hn.hn_kv_cache_reset(c)
+    torch.cuda.synchronize()
+    reps = 4 * n_sets
+    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        c, kv = sets[i % n_sets]
+        hn.hn_kv_cache_reset(c)
+        e0[i].record(stream)
+        hn.hn_kv_quant_append(c, seg0, *kv)
+        e1[i].record(stream)
+    torch.cuda.synchronize()
+    app_ms = sorted(a.elapsed_time(b) for a, b in zip(e0, e1))
+    app_med = app_ms[len(app_ms) // 2]
+    append_gbs = append_bytes / (app_med * 1e-3) / 1e9
+
+    traffic = None
+    if args.traffic:
+        t = json.loads(args.traffic)
+        traffic = (t["fetch_kib"] + t["write_kib"]) * 1024 * t.get("scale", 1.0)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": {
+                "c2": "480x832 single segment: 16 heads x 128, 30 latent frames x 390 tokens "
+                      "= 11,700 video queries, 768-token head + 4 x 128-token action tails, no history",
+                "c3": "1280x704 steady state: 26,400 queries, INT8 ring of 18 frames (15,840 tokens) "
+                      "+ 3 x 768 cached heads, own 768 + 4 x 128 text",
+                "c4": "1280x704 7th segment, no window: 26,400 queries, INT8 history of 158,400 video "
+                      "tokens + 6 x 1,280 heads, Student-t keys/values",
+                "c5": "480x832 single segment, block-sparse: 25% of video tiles kept per query tile",
+            }.get(args.workload, args.workload),
+            "name": args.workload,
+            "step": "tile plan + attention + INT8 quantize/append",
+            "effective_flop_per_step": flops,
+            "visible_pairs_per_head": pairs,
+        },
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "roofline": {
+            "kernel": "seg_attn_fwd_kernel",
+            "bound": "mfma",
+            "achieved": round(achieved, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "avg_launch_ms": round(attn_avg, 4),
+        },
+        "append": {
+            "kernel": "quant_append_kernel",
+            "bound": "hbm",
+            "bytes": append_bytes,
+            "median_ms": round(app_med, 4),
+            "achieved": round(append_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(append_gbs / PEAK_HBM_GBS, 4),
+            "rotating_sets": n_sets,
+        },
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = np.linspace(0, w.current.video_len - 1, min(args.cpu_rows, w.current.video_len)).astype(int)
+        rows = np.unique(rows)
+        tc0 = time.perf_counter()
+        oracle.attention(w, data, rows)
+        tc = time.perf_counter() - tc0
+        if csr is None:
+            per_row = pairs / w.current.video_len
+            sample_pairs = per_row * len(rows)
+        else:
+            sample_pairs = pairs * len(rows) / w.current.video_len
+        cpu_tflops = 4.0 * 128 * sample_pairs * w.heads / tc / 1e12
+        ncores = len(os.sched_getaffinity(0))
+        out["cpu_baseline"] = {
+            "value": round(cpu_tflops, 6),
+            "unit": "TFLOP/s",
+            "cores": ncores,
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {w.current.video_len} query rows (evenly spaced), all "
+                      f"{w.heads} heads, fp64 numpy oracle incl. key preparation; {tc:.1f} s",
+        }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

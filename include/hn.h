@@ -1,0 +1,264 @@
+/*
+ * hn.h - segment-causal, action-aware attention over an INT8 sliding-window
+ * KV cache, for one AMD Instinct MI355X (gfx950).
+ *
+ * The method is the attention of the Hy-Nomas segment-autoregressive MMDiT
+ * as described on these pages:
+ *   [T] fluxbbs.com, "Hy-Nomas 拆解：8B 世界模型用 20.53 GiB 显存跑 100 秒"
+ *       (section "架构" = architecture; "单卡 4090 怎么做到的" = how one 4090
+ *       does it; "训练流程" = training)
+ *   [H] hyphentech.top, "腾讯 Hy-Nomas 开放权重：一张 RTX 4090 能跑怎样的交互式视频世界？"
+ *       (section "标准方案和单卡方案不是同一套成本", its configuration table
+ *       and the warning under it)
+ *   [G] papers.ananclaw.com, "Hy-Nomas：腾讯混元开源的自由交互世界生成模型 · 干货攻略"
+ *       (section "这是什么" = what it is: model-card architecture and method
+ *       paragraph; "离线 prompt JSON 格式" = prompt JSON format)
+ *
+ * Conventions shared by every entry point
+ *  - Every function returns hn_status; HN_OK (0) on success.  Nothing prints,
+ *    throws or exits.  On failure hn_last_error() holds a message for the
+ *    calling thread.
+ *  - All argument checks happen on the host before anything is enqueued.  A
+ *    call that fails enqueues no GPU work and leaves the cache counters
+ *    unchanged.  Kernel launch failures map to HN_ERR_HIP.  Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Device buffers are allocated by the caller, must stay alive until the
+ *    enqueued work completes, and are never freed by the library.  The
+ *    library allocates no device memory and never synchronises the stream.
+ *  - bf16 tensors supplied by the caller are token-major [tokens][H][D],
+ *    rows contiguous, D = HN_HEAD_DIM = 128 (the MMDiT uses 16 heads of 128
+ *    dims: [G] "这是什么", architecture bullet).  The INT8 cache is the
+ *    library's own head-major layout (below).
+ *  - Work runs on the given HIP stream (0 = the null stream).
+ *  - Outputs are bitwise reproducible from run to run: tile order is fixed
+ *    and no reduction uses atomics.
+ */
+#ifndef HN_H
+#define HN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HN_HEAD_DIM 128
+#define HN_MAX_ACTIONS 64   /* action tails per segment */
+#define HN_TILE 128         /* query/key tile of block-sparse keep lists */
+
+typedef enum {
+  HN_OK = 0,
+  HN_ERR_NULL = 1,         /* a required pointer is NULL */
+  HN_ERR_INVALID = 2,      /* inconsistent sizes or layout */
+  HN_ERR_UNSUPPORTED = 3,  /* valid but not supported (e.g. head_dim != 128) */
+  HN_ERR_CAPACITY = 4,     /* description-head store or buffer too small */
+  HN_ERR_WORKSPACE = 5,    /* workspace / output buffer too small */
+  HN_ERR_ORDER = 6,        /* segment order or stale tile plan */
+  HN_ERR_HIP = 7           /* a HIP runtime call failed */
+} hn_status;
+
+const char* hn_status_string(hn_status s);
+/* Message of the last failing call made by this thread ("" if none). */
+const char* hn_last_error(void);
+
+/* Token layout of the current segment (host memory, read during the call).
+ *
+ * A segment carries text then video.  Its text is one description head,
+ * visible to every later segment, followed by m action tails; tail j is
+ * visible only to this segment's video queries whose latent frame lies in
+ * its time window ([T] "架构", action-aware causal attention; [G] prompt
+ * JSON: each segment lists contained_actions with start/end times).
+ * Text rows are ordered head, tail_0 .. tail_{m-1}; video rows are
+ * frame-major, tokens_per_frame tokens per latent frame.
+ * Windows are half-open in local latent frames: 0 <= f0 <= f1 <= frames.
+ */
+typedef struct hn_seg_layout {
+  int32_t index;              /* 0-based segment index; must equal cache->segments */
+  int32_t frames;             /* F latent frames (>= 1) */
+  int32_t tokens_per_frame;   /* P, must equal cache->tokens_per_frame */
+  int32_t head_len;           /* h description-head tokens (>= 0) */
+  int32_t num_actions;        /* m action tails (0 .. HN_MAX_ACTIONS) */
+  int32_t reserved0;
+  const int32_t* action_len;  /* [m] tokens per tail (>= 0) */
+  const int32_t* action_f0;   /* [m] first latent frame of the window */
+  const int32_t* action_f1;   /* [m] one past the last latent frame */
+} hn_seg_layout;
+
+/* The INT8 KV cache of earlier segments.
+ *
+ * Keys and values are stored as INT8 with one fp32 scale per (token, head)
+ * and used in BF16 ([T] "单卡 4090 怎么做到的", first technique).  Video of
+ * earlier segments lives in a ring of W latent frames, oldest frame evicted
+ * first ([T] same section, second technique: 18 history frames; [H]
+ * configuration table, history row).  Description heads of every earlier
+ * segment live in a separate head store, since heads stay visible across
+ * segments ([T] "架构").  Tails are never stored: no later segment sees them.
+ *
+ * Device buffers (caller-allocated; sizes from hn_kv_cache_sizes):
+ *   ring_k, ring_v   int8  [H][W*P][D]   token t of ring slot s at row s*P+t
+ *   ring_ks, ring_vs fp32  [H][W*P]
+ *   heads_k, heads_v int8  [H][head_cap][D], heads of segments 0,1,.. in order
+ *   heads_ks, heads_vs fp32 [H][head_cap]
+ * Global latent frame g (frames of all earlier segments + local frame) lives
+ * in ring slot g mod W.  The counters are host-side and updated by
+ * hn_kv_quant_append; zero them (or call hn_kv_cache_reset) for a new video.
+ * The whole struct is plain data: saving it and the buffers saves the cache.
+ * With no window, give W >= the total number of latent frames.
+ */
+typedef struct hn_kv_cache {
+  int32_t num_heads;          /* H >= 1 */
+  int32_t head_dim;           /* D, must be 128 */
+  int32_t tokens_per_frame;   /* P >= 1 */
+  int32_t window_frames;      /* W >= 1, ring capacity in latent frames */
+  int32_t head_cap_tokens;    /* head-store capacity in tokens (>= 0) */
+  int32_t reserved0;
+  int8_t* ring_k;
+  int8_t* ring_v;
+  float* ring_ks;
+  float* ring_vs;
+  int8_t* heads_k;
+  int8_t* heads_v;
+  float* heads_ks;
+  float* heads_vs;
+  int64_t frames_seen;        /* latent frames appended so far */
+  int32_t head_tokens;        /* valid tokens in the head store */
+  int32_t segments;           /* segments appended so far */
+} hn_kv_cache;
+
+/* Bytes of each cache buffer for the given shape (any output may be NULL). */
+hn_status hn_kv_cache_sizes(int32_t num_heads, int32_t window_frames, int32_t tokens_per_frame,
+                            int32_t head_cap_tokens, size_t* ring_bytes, size_t* ring_scale_bytes,
+                            size_t* heads_bytes, size_t* heads_scale_bytes);
+/* Zero the counters (frames_seen, head_tokens, segments); buffers untouched. */
+hn_status hn_kv_cache_reset(hn_kv_cache* cache);
+
+/* Quantize the current segment's keys/values and append them to the cache.
+ *
+ * Per (token, head) row x of 128 bf16 values, in IEEE fp32:
+ *   amax = max|x_i|;  scale = amax / 127 (correctly rounded);
+ *   q_i = round_half_even(x_i / scale) (correctly rounded quotient), clamped
+ *   to [-127, 127]; a row with amax == 0 stores scale 0 and q 0.
+ * (The pages state INT8 storage with float scales only, [T] first
+ * technique; this formula is the library's reading of it.)
+ * Written: the head rows [0, h) of k_txt/v_txt into the head store at
+ * [head_tokens, head_tokens + h); the last min(F, W) latent frames of
+ * k_vid/v_vid into ring slots (frames_seen + f) mod W.  Frames the window
+ * drops at once, and the action tails, are not read.
+ * Then frames_seen += F, head_tokens += h, segments += 1.
+ *
+ * k_txt, v_txt : bf16 [h + sum(a)][H][D] (device); may be NULL if h == 0
+ * k_vid, v_vid : bf16 [F*P][H][D] (device)
+ * Errors: HN_ERR_ORDER if seg->index != cache->segments; HN_ERR_CAPACITY if
+ * the head store would overflow; HN_ERR_INVALID on inconsistent shapes.
+ * Call it after every hn_seg_attn_fwd of the segment (the cache must not
+ * yet hold the segment the queries belong to).
+ */
+hn_status hn_kv_quant_append(hn_kv_cache* cache, const hn_seg_layout* seg,
+                             const void* k_txt, const void* v_txt,
+                             const void* k_vid, const void* v_vid,
+                             hipStream_t stream);
+
+/* Optional block-sparse keep list (device memory, caller-owned).
+ *
+ * After the first two denoising steps only 25% of the candidate video blocks
+ * are kept ([T] "单卡 4090 怎么做到的", fourth technique).  Query tiles are
+ * HN_TILE rows of the segment's video queries; video key tiles are HN_TILE
+ * tokens, numbered first over the history video still in the window (oldest
+ * frame first, ragged last tile), then over the segment's own video (ragged
+ * last tile).  Row t of the CSR lists the video tiles query tile t keeps, in
+ * strictly increasing order; ids out of range, repeated or out of order are
+ * skipped.  Text (heads and visible tails) is always kept.
+ */
+typedef struct hn_block_sparse {
+  int32_t tile_q;             /* must be HN_TILE */
+  int32_t tile_k;             /* must be HN_TILE */
+  int32_t n_qtiles;           /* must be ceil(F*P / HN_TILE) */
+  int32_t reserved0;
+  const int32_t* row_ptr;     /* [n_qtiles + 1], row_ptr[0] = 0, non-decreasing */
+  const int32_t* col;         /* [row_ptr[n_qtiles]] video tile ids */
+} hn_block_sparse;
+
+typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
+
+/* Tile plan for one (cache state, segment, keep list); filled by
+ * hn_attn_mask_build in TILE_PLAN mode and consumed by hn_seg_attn_fwd.
+ * It may be reused by every attention call of the segment (all blocks and
+ * denoising steps with the same keep list). */
+typedef struct hn_tile_plan {
+  const void* dev;            /* = the workspace the plan was written to */
+  int32_t tile_q;             /* query rows per plan tile */
+  int32_t n_qtiles;
+  int32_t max_spans;          /* span slots per query tile */
+  int32_t seg_index;          /* cache/segment state the plan was built for */
+  int64_t frames_seen;
+  int32_t head_tokens;
+  int32_t sparse;             /* 1 if a keep list was merged */
+  int64_t visible_pairs;      /* unmasked (query, key) pairs per head; -1 if sparse */
+} hn_tile_plan;
+
+/* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments). */
+size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg,
+                              const hn_block_sparse* sparse);
+
+/* Build the attention mask of the current segment's video queries.
+ *
+ * Visibility of key k for the video query at local frame f
+ * ([T] "架构": segment-causal and action-aware attention; [H] warning under
+ * the table: the window bounds history only):
+ *   earlier segment's head            : always
+ *   earlier segment's tails           : never (not in the cache)
+ *   earlier video in the ring window  : always (evicted frames: never)
+ *   own head                          : always
+ *   own tail j                        : iff action_f0[j] <= f < action_f1[j]
+ *   own video                         : always (bidirectional in a segment)
+ *   later segments                    : never (not in the cache yet)
+ *   with a keep list: video keys only in the query tile's kept tiles.
+ *
+ * TILE_PLAN: `out` is the workspace (>= hn_attn_workspace_size bytes, device,
+ *   16-byte aligned).  For every query tile a kernel writes the list of key
+ *   spans to visit, each classified against the tile's rows as full or
+ *   partial (a row range then restricts it); empty spans are dropped.  `plan`
+ *   is filled.  row0/nrows are ignored.
+ * DENSE: `out` is uint8 [nrows][Lk] (device) for query rows
+ *   [row0, row0 + nrows), in the canonical key order
+ *   [history heads, oldest segment first | history video in the window,
+ *    oldest frame first | own head | own tails | own video],
+ *   Lk = head_tokens + kept_frames*P + h + sum(a) + F*P; 1 = visible.  It is
+ *   expanded from the same span lists (a debugging and test view).  `plan`
+ *   must be NULL.
+ */
+hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
+                             const hn_block_sparse* sparse, hn_mask_mode mode,
+                             int32_t row0, int32_t nrows, void* out, size_t out_bytes,
+                             hn_tile_plan* plan, hipStream_t stream);
+
+/* Attention of the current segment's video queries over the cache and the
+ * segment's own text and video, with one softmax over the union of visible
+ * keys (the mask of hn_attn_mask_build):
+ *   O[q] = sum_k softmax_k(sm_scale * Q[q].K[k]) V[k]
+ * History keys/values are the dequantized INT8 values q*scale; the segment's
+ * own keys/values are used as given (quantization is storage-only,
+ * [T] "单卡 4090 怎么做到的", first technique).  BF16 MFMA, fp32 accumulation
+ * and online softmax.
+ *
+ * plan         : from hn_attn_mask_build(TILE_PLAN) for this exact cache
+ *                state and segment, workspace still intact; else HN_ERR_ORDER
+ * q_vid        : bf16 [F*P][H][D]
+ * k_txt, v_txt : bf16 [h + sum(a)][H][D] (may be NULL if h + sum(a) == 0)
+ * k_vid, v_vid : bf16 [F*P][H][D]
+ * o_vid        : bf16 [F*P][H][D] (output; must not alias the inputs)
+ * lse          : fp32 [H][F*P] natural-log softmax normaliser, or NULL
+ * sm_scale     : score scale, normally 1/sqrt(128)
+ */
+hn_status hn_seg_attn_fwd(const hn_kv_cache* cache, const hn_seg_layout* seg,
+                          const hn_tile_plan* plan, const void* q_vid,
+                          const void* k_txt, const void* v_txt,
+                          const void* k_vid, const void* v_vid,
+                          void* o_vid, float* lse, float sm_scale, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HN_H */

@@ -1,0 +1,333 @@
+// Host side of the C ABI: argument checks, cache bookkeeping, launches.
+//
+// Every check runs before anything is enqueued; a failing call leaves the
+// cache counters untouched.  Nothing here allocates device memory or
+// synchronises a stream.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "hn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+hn_status fail(hn_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+hn_status ok() {
+  g_err[0] = '\0';
+  return HN_OK;
+}
+
+hn_status check_cache(const hn_kv_cache* c) {
+  if (!c) return fail(HN_ERR_NULL, "cache is NULL");
+  if (c->head_dim != HN_HEAD_DIM)
+    return fail(HN_ERR_UNSUPPORTED, "head_dim %d unsupported (only %d)", c->head_dim, HN_HEAD_DIM);
+  if (c->num_heads < 1) return fail(HN_ERR_INVALID, "num_heads %d < 1", c->num_heads);
+  if (c->tokens_per_frame < 1) return fail(HN_ERR_INVALID, "tokens_per_frame %d < 1", c->tokens_per_frame);
+  if (c->window_frames < 1) return fail(HN_ERR_INVALID, "window_frames %d < 1", c->window_frames);
+  if (c->head_cap_tokens < 0) return fail(HN_ERR_INVALID, "head_cap_tokens %d < 0", c->head_cap_tokens);
+  if ((int64_t)c->window_frames * c->tokens_per_frame > INT_MAX / 2)
+    return fail(HN_ERR_UNSUPPORTED, "ring of %d x %d tokens too large", c->window_frames, c->tokens_per_frame);
+  if (c->frames_seen < 0 || c->head_tokens < 0 || c->segments < 0 || c->head_tokens > c->head_cap_tokens)
+    return fail(HN_ERR_INVALID, "cache counters are inconsistent");
+  if (!c->ring_k || !c->ring_v || !c->ring_ks || !c->ring_vs)
+    return fail(HN_ERR_NULL, "cache ring buffers are NULL");
+  if (c->head_cap_tokens > 0 && (!c->heads_k || !c->heads_v || !c->heads_ks || !c->heads_vs))
+    return fail(HN_ERR_NULL, "cache head-store buffers are NULL");
+  return HN_OK;
+}
+
+hn_status check_seg(const hn_kv_cache* c, const hn_seg_layout* s, int64_t* text_len) {
+  if (!s) return fail(HN_ERR_NULL, "segment layout is NULL");
+  if (s->frames < 1) return fail(HN_ERR_INVALID, "frames %d < 1", s->frames);
+  if (s->tokens_per_frame != c->tokens_per_frame)
+    return fail(HN_ERR_INVALID, "segment tokens_per_frame %d != cache %d", s->tokens_per_frame,
+                c->tokens_per_frame);
+  if ((int64_t)s->frames * s->tokens_per_frame > INT_MAX / 2)
+    return fail(HN_ERR_UNSUPPORTED, "segment of %d x %d tokens too large", s->frames, s->tokens_per_frame);
+  if (s->head_len < 0) return fail(HN_ERR_INVALID, "head_len %d < 0", s->head_len);
+  if (s->num_actions < 0 || s->num_actions > HN_MAX_ACTIONS)
+    return fail(HN_ERR_UNSUPPORTED, "num_actions %d outside [0, %d]", s->num_actions, HN_MAX_ACTIONS);
+  if (s->num_actions > 0 && (!s->action_len || !s->action_f0 || !s->action_f1))
+    return fail(HN_ERR_NULL, "action arrays are NULL");
+  int64_t tl = s->head_len;
+  for (int j = 0; j < s->num_actions; ++j) {
+    if (s->action_len[j] < 0) return fail(HN_ERR_INVALID, "action %d has length %d", j, s->action_len[j]);
+    if (s->action_f0[j] < 0 || s->action_f0[j] > s->action_f1[j] || s->action_f1[j] > s->frames)
+      return fail(HN_ERR_INVALID, "action %d window [%d, %d) not inside [0, %d]", j, s->action_f0[j],
+                  s->action_f1[j], s->frames);
+    tl += s->action_len[j];
+  }
+  if (tl > INT_MAX / 2) return fail(HN_ERR_UNSUPPORTED, "text of %lld tokens too large", (long long)tl);
+  *text_len = tl;
+  return HN_OK;
+}
+
+int kept_frames(const hn_kv_cache* c) {
+  return (int)std::min<int64_t>(c->frames_seen, c->window_frames);
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Plan parameters for the current state; validates the keep list.
+hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
+                           hn::PlanParams* pp) {
+  int64_t tl = 0;
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  std::memset(pp, 0, sizeof(*pp));
+  const int P = c->tokens_per_frame;
+  const int lq = s->frames * P;
+  pp->tile_q = HN_TILE;
+  pp->n_qtiles = (int)ceil_div(lq, HN_TILE);
+  pp->lq = lq;
+  pp->P = P;
+  pp->head_tokens = c->head_tokens;
+  const int kf = kept_frames(c);
+  pp->kept_frames = kf;
+  pp->ring_tokens = kf * P;
+  pp->ring_rot = (int)(((c->frames_seen - kf) % c->window_frames) * P);
+  pp->head_len = s->head_len;
+  pp->text_len = (int)tl;
+  pp->m = s->num_actions;
+  int off = s->head_len;
+  for (int j = 0; j < s->num_actions; ++j) {
+    pp->tail_off[j] = off;
+    pp->tail_len[j] = s->action_len[j];
+    pp->tail_f0[j] = s->action_f0[j];
+    pp->tail_f1[j] = s->action_f1[j];
+    off += s->action_len[j];
+  }
+  pp->n_hist_tiles = (int)ceil_div(pp->ring_tokens, HN_TILE);
+  pp->n_own_tiles = pp->n_qtiles;
+  int max_spans = 4 + s->num_actions;
+  if (sp) {
+    if (sp->tile_q != HN_TILE || sp->tile_k != HN_TILE)
+      return fail(HN_ERR_UNSUPPORTED, "block-sparse tiles %dx%d unsupported (only %d)", sp->tile_q,
+                  sp->tile_k, HN_TILE);
+    if (sp->n_qtiles != pp->n_qtiles)
+      return fail(HN_ERR_INVALID, "block-sparse n_qtiles %d != %d", sp->n_qtiles, pp->n_qtiles);
+    if (!sp->row_ptr || !sp->col) return fail(HN_ERR_NULL, "block-sparse arrays are NULL");
+    pp->sparse = 1;
+    pp->row_ptr = sp->row_ptr;
+    pp->col = sp->col;
+    // every kept tile may become its own span; one history tile may wrap the ring
+    max_spans = 4 + s->num_actions + pp->n_hist_tiles + 1 + pp->n_own_tiles;
+  }
+  pp->max_spans = max_spans;
+  return HN_OK;
+}
+
+hn_status hip_fail(hipError_t e, const char* what) {
+  return fail(HN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hn_status_string(hn_status s) {
+  switch (s) {
+    case HN_OK: return "ok";
+    case HN_ERR_NULL: return "null pointer";
+    case HN_ERR_INVALID: return "invalid argument";
+    case HN_ERR_UNSUPPORTED: return "unsupported";
+    case HN_ERR_CAPACITY: return "capacity exceeded";
+    case HN_ERR_WORKSPACE: return "workspace too small";
+    case HN_ERR_ORDER: return "segment order or stale plan";
+    case HN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* hn_last_error(void) { return g_err; }
+
+hn_status hn_kv_cache_sizes(int32_t H, int32_t W, int32_t P, int32_t cap, size_t* ring_bytes,
+                            size_t* ring_scale_bytes, size_t* heads_bytes, size_t* heads_scale_bytes) {
+  if (H < 1 || W < 1 || P < 1 || cap < 0) return fail(HN_ERR_INVALID, "invalid cache shape");
+  const size_t ring = (size_t)H * W * P;
+  if (ring_bytes) *ring_bytes = ring * HN_HEAD_DIM;
+  if (ring_scale_bytes) *ring_scale_bytes = ring * sizeof(float);
+  if (heads_bytes) *heads_bytes = (size_t)H * cap * HN_HEAD_DIM;
+  if (heads_scale_bytes) *heads_scale_bytes = (size_t)H * cap * sizeof(float);
+  return ok();
+}
+
+hn_status hn_kv_cache_reset(hn_kv_cache* c) {
+  if (!c) return fail(HN_ERR_NULL, "cache is NULL");
+  c->frames_seen = 0;
+  c->head_tokens = 0;
+  c->segments = 0;
+  return ok();
+}
+
+hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void* k_txt,
+                             const void* v_txt, const void* k_vid, const void* v_vid,
+                             hipStream_t stream) {
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  int64_t tl = 0;
+  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  if (s->index != c->segments)
+    return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
+  if (!k_vid || !v_vid) return fail(HN_ERR_NULL, "k_vid/v_vid is NULL");
+  if (s->head_len > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
+  if ((int64_t)c->head_tokens + s->head_len > c->head_cap_tokens)
+    return fail(HN_ERR_CAPACITY, "head store holds %d of %d tokens; %d more do not fit", c->head_tokens,
+                c->head_cap_tokens, s->head_len);
+  const int P = c->tokens_per_frame;
+  const int surv = std::min(s->frames, c->window_frames);
+  hn::AppendParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.H = c->num_heads;
+  p.head_len = s->head_len;
+  p.vid_frame0 = s->frames - surv;
+  p.vid_first = p.vid_frame0 * P;
+  p.n_vid = surv * P;
+  p.P = P;
+  p.W = c->window_frames;
+  p.frames_seen = c->frames_seen;
+  p.head_pos = c->head_tokens;
+  p.head_cap = c->head_cap_tokens;
+  p.ring_cap = c->window_frames * P;
+  p.k_txt = static_cast<const __bf16*>(k_txt);
+  p.v_txt = static_cast<const __bf16*>(v_txt);
+  p.k_vid = static_cast<const __bf16*>(k_vid);
+  p.v_vid = static_cast<const __bf16*>(v_vid);
+  p.ring_k = c->ring_k; p.ring_v = c->ring_v; p.ring_ks = c->ring_ks; p.ring_vs = c->ring_vs;
+  p.heads_k = c->heads_k; p.heads_v = c->heads_v; p.heads_ks = c->heads_ks; p.heads_vs = c->heads_vs;
+  hipError_t e = hn::launch_quant_append(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "quant_append launch");
+  c->frames_seen += s->frames;
+  c->head_tokens += s->head_len;
+  c->segments += 1;
+  return ok();
+}
+
+size_t hn_attn_workspace_size(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp) {
+  hn::PlanParams pp;
+  if (make_plan_params(c, s, sp, &pp) != HN_OK) return 0;
+  return hn::plan_bytes(pp.n_qtiles, pp.max_spans);
+}
+
+hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
+                             hn_mask_mode mode, int32_t row0, int32_t nrows, void* out, size_t out_bytes,
+                             hn_tile_plan* plan, hipStream_t stream) {
+  hn::PlanParams pp;
+  hn_status st = make_plan_params(c, s, sp, &pp);
+  if (st != HN_OK) return st;
+  if (!out) return fail(HN_ERR_NULL, "output buffer is NULL");
+  if (mode == HN_MASK_TILE_PLAN) {
+    if (!plan) return fail(HN_ERR_NULL, "plan is NULL");
+    if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return fail(HN_ERR_INVALID, "workspace not 16-byte aligned");
+    const size_t need = hn::plan_bytes(pp.n_qtiles, pp.max_spans);
+    if (out_bytes < need)
+      return fail(HN_ERR_WORKSPACE, "workspace of %zu bytes; %zu needed", out_bytes, need);
+    hipError_t e = hn::launch_plan(pp, out, stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    plan->dev = out;
+    plan->tile_q = pp.tile_q;
+    plan->n_qtiles = pp.n_qtiles;
+    plan->max_spans = pp.max_spans;
+    plan->seg_index = s->index;
+    plan->frames_seen = c->frames_seen;
+    plan->head_tokens = c->head_tokens;
+    plan->sparse = pp.sparse;
+    if (pp.sparse) {
+      plan->visible_pairs = -1;
+    } else {
+      int64_t pairs = 0;
+      const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
+      for (int f = 0; f < s->frames; ++f) {
+        int64_t n = base;
+        for (int j = 0; j < s->num_actions; ++j)
+          if (s->action_f0[j] <= f && f < s->action_f1[j]) n += s->action_len[j];
+        pairs += n * pp.P;
+      }
+      plan->visible_pairs = pairs;
+    }
+    return ok();
+  }
+  if (mode != HN_MASK_DENSE) return fail(HN_ERR_INVALID, "unknown mask mode %d", (int)mode);
+  if (plan) return fail(HN_ERR_INVALID, "plan must be NULL in DENSE mode");
+  if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > pp.lq)
+    return fail(HN_ERR_INVALID, "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, pp.lq);
+  if ((size_t)pp.max_spans * sizeof(hn::Span) > 64 * 1024)
+    return fail(HN_ERR_UNSUPPORTED, "%d spans per tile exceed the dense expander's LDS", pp.max_spans);
+  hn::DenseParams d;
+  std::memset(&d, 0, sizeof(d));
+  d.plan = pp;
+  d.row0 = row0;
+  d.nrows = nrows;
+  d.lk = (int64_t)pp.head_tokens + pp.ring_tokens + pp.text_len + pp.lq;
+  d.W = c->window_frames;
+  d.frames_seen = c->frames_seen;
+  d.out = static_cast<uint8_t*>(out);
+  if (out_bytes < (size_t)nrows * (size_t)d.lk)
+    return fail(HN_ERR_WORKSPACE, "dense mask needs %zu bytes; %zu given", (size_t)nrows * (size_t)d.lk,
+                out_bytes);
+  hipError_t e = hn::launch_dense(d, stream);
+  if (e != hipSuccess) return hip_fail(e, "dense mask launch");
+  return ok();
+}
+
+hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn_tile_plan* plan,
+                          const void* q_vid, const void* k_txt, const void* v_txt, const void* k_vid,
+                          const void* v_vid, void* o_vid, float* lse, float sm_scale, hipStream_t stream) {
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  int64_t tl = 0;
+  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  if (!plan || !plan->dev) return fail(HN_ERR_NULL, "plan is NULL");
+  if (s->index != c->segments)
+    return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
+  const int P = c->tokens_per_frame;
+  const int lq = s->frames * P;
+  if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
+      plan->head_tokens != c->head_tokens || plan->tile_q != HN_TILE ||
+      plan->n_qtiles != (int)ceil_div(lq, HN_TILE))
+    return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
+  if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
+  if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
+  if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
+  hn::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.H = c->num_heads;
+  p.lq = lq;
+  p.n_qtiles = plan->n_qtiles;
+  p.max_spans = plan->max_spans;
+  p.n_tasks = p.H * p.n_qtiles;
+  p.tasks_per_xcd = (p.n_tasks + 7) / 8;
+  p.head_cap = c->head_cap_tokens;
+  p.ring_cap = c->window_frames * P;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.counts = static_cast<const int32_t*>(plan->dev);
+  p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
+                                              hn::plan_counts_bytes(plan->n_qtiles));
+  p.q = static_cast<const __bf16*>(q_vid);
+  p.k_txt = static_cast<const __bf16*>(k_txt);
+  p.v_txt = static_cast<const __bf16*>(v_txt);
+  p.k_vid = static_cast<const __bf16*>(k_vid);
+  p.v_vid = static_cast<const __bf16*>(v_vid);
+  p.heads_k = c->heads_k; p.heads_v = c->heads_v; p.heads_ks = c->heads_ks; p.heads_vs = c->heads_vs;
+  p.ring_k = c->ring_k; p.ring_v = c->ring_v; p.ring_ks = c->ring_ks; p.ring_vs = c->ring_vs;
+  p.o = static_cast<__bf16*>(o_vid);
+  p.lse = lse;
+  hipError_t e = hn::launch_attn(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return ok();
+}
+
+}  // extern "C"

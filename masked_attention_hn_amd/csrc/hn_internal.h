@@ -1,0 +1,142 @@
+// Internal types shared by the host layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "hn.h"
+
+namespace hn {
+
+constexpr int D = HN_HEAD_DIM;
+constexpr int TILE = HN_TILE;
+
+// Key sources an attention span can come from.
+enum Src : int32_t {
+  SRC_HEADS = 0,  // INT8 head store (description heads of earlier segments)
+  SRC_RING = 1,   // INT8 video ring (history frames still in the window), slot order
+  SRC_TXT = 2,    // bf16 text rows of the current segment (head, tails)
+  SRC_VID = 3,    // bf16 video rows of the current segment
+};
+
+// One contiguous run of keys of one source, visited by one query tile.
+// Query rows outside [r0, r1) must not see it (action-tail window).
+struct __attribute__((aligned(16))) Span {
+  int32_t src;
+  int32_t k0, k1;   // key range inside the source
+  int32_t r0, r1;   // visible query rows [r0, r1) (segment-local video rows)
+  int32_t full;     // 1 if every row of the query tile is inside [r0, r1)
+  int32_t pad0, pad1;
+};
+static_assert(sizeof(Span) == 32, "Span layout");
+
+// Everything the span builder needs; passed by value to kernels.
+struct PlanParams {
+  int32_t n_qtiles;
+  int32_t tile_q;
+  int32_t lq;            // F*P video queries
+  int32_t P;
+  int32_t max_spans;
+  int32_t head_tokens;   // history heads in the head store
+  int32_t kept_frames;   // history frames in the ring window
+  int32_t ring_rot;      // slot-space offset (tokens) of the oldest kept frame
+  int32_t ring_tokens;   // kept_frames * P
+  int32_t head_len;      // own head h
+  int32_t text_len;      // h + sum(a)
+  int32_t m;             // tails
+  int32_t tail_off[HN_MAX_ACTIONS];
+  int32_t tail_len[HN_MAX_ACTIONS];
+  int32_t tail_f0[HN_MAX_ACTIONS];
+  int32_t tail_f1[HN_MAX_ACTIONS];
+  // block sparsity
+  int32_t sparse;
+  int32_t n_hist_tiles;
+  int32_t n_own_tiles;
+  int32_t pad0;
+  const int32_t* row_ptr;
+  const int32_t* col;
+};
+
+// Workspace layout of a tile plan: int32 count[n_qtiles] padded to 256 bytes,
+// then Span spans[n_qtiles][max_spans].
+inline size_t plan_counts_bytes(int n_qtiles) {
+  size_t b = (size_t)n_qtiles * sizeof(int32_t);
+  return (b + 255) & ~(size_t)255;
+}
+inline size_t plan_bytes(int n_qtiles, int max_spans) {
+  return plan_counts_bytes(n_qtiles) + (size_t)n_qtiles * max_spans * sizeof(Span);
+}
+
+struct AttnParams {
+  int32_t H;
+  int32_t lq;
+  int32_t n_qtiles;
+  int32_t max_spans;
+  int32_t n_tasks;
+  int32_t tasks_per_xcd;
+  int32_t head_cap;      // head-store stride (tokens) per head
+  int32_t ring_cap;      // ring stride (tokens) per head = W*P
+  float scale_log2;      // sm_scale * log2(e)
+  int32_t pad0;
+  const int32_t* counts;
+  const Span* spans;
+  const __bf16* q;
+  const __bf16* k_txt;
+  const __bf16* v_txt;
+  const __bf16* k_vid;
+  const __bf16* v_vid;
+  const int8_t* heads_k;
+  const int8_t* heads_v;
+  const float* heads_ks;
+  const float* heads_vs;
+  const int8_t* ring_k;
+  const int8_t* ring_v;
+  const float* ring_ks;
+  const float* ring_vs;
+  __bf16* o;
+  float* lse;
+};
+
+struct AppendParams {
+  int32_t H;
+  int32_t head_len;       // head rows to store
+  int32_t vid_first;      // first video row read (first surviving frame * P)
+  int32_t n_vid;          // surviving video rows
+  int32_t P;
+  int32_t W;
+  int64_t frames_seen;    // before this append
+  int32_t head_pos;       // head-store row of the first new head token
+  int32_t head_cap;
+  int32_t ring_cap;       // W*P
+  int32_t vid_frame0;     // local frame of vid_first
+  const __bf16* k_txt;
+  const __bf16* v_txt;
+  const __bf16* k_vid;
+  const __bf16* v_vid;
+  int8_t* ring_k;
+  int8_t* ring_v;
+  float* ring_ks;
+  float* ring_vs;
+  int8_t* heads_k;
+  int8_t* heads_v;
+  float* heads_ks;
+  float* heads_vs;
+};
+
+struct DenseParams {
+  PlanParams plan;
+  int32_t row0, nrows;
+  int64_t lk;             // columns
+  int32_t W;
+  int32_t pad0;
+  int64_t frames_seen;
+  uint8_t* out;
+};
+
+// Launchers (defined next to their kernels); return the HIP error of the launch.
+hipError_t launch_quant_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s);
+hipError_t launch_dense(const DenseParams& p, hipStream_t s);
+hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+
+}  // namespace hn

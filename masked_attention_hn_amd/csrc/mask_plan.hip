@@ -1,0 +1,185 @@
+// Tile plan (per query tile: the key spans to visit) and its dense expansion.
+//
+// Visibility rules ("Hy-Nomas 拆解" teardown, section "架构"): inside a segment
+// attention is bidirectional; a segment sees itself and earlier segments only;
+// each segment's text is a description head, visible across segments, and
+// action tails visible only inside their own segment and time window.  The
+// history window bounds earlier video only, never the current segment
+// (hyphentech explainer, warning under the configuration table).  With a keep
+// list, video keys outside the query tile's kept 128-token tiles are dropped
+// (teardown, "单卡 4090 怎么做到的", fourth technique).
+//
+// The spans of one query tile, in visiting order:
+//   earlier description heads | history video in the window (ring slot order,
+//   or the kept tiles, oldest first, when sparse) | own head | own tails |
+//   own video (or its kept tiles).
+// Each span is classified against the query tile's rows: tails whose window
+// covers every row are full, tails covering none are dropped, the rest are
+// partial and carry their row range [f0*P, f1*P).  Adjacent spans of the same
+// source that are both full (or share a row range) are merged, so a dense plan
+// has at most 4 + m spans per tile.
+#include <climits>
+
+#include "hn_internal.h"
+
+namespace hn {
+namespace {
+
+struct SpanWriter {
+  Span* out;
+  int n;
+  int cap;
+  int R0, R1;  // rows of the query tile
+
+  __device__ void emit(int src, int k0, int k1, int r0, int r1) {
+    if (k1 <= k0) return;
+    const int a = max(r0, R0), b = min(r1, R1);
+    if (a >= b) return;  // no row of this tile sees it
+    const int full = (r0 <= R0 && R1 <= r1) ? 1 : 0;
+    if (full) { r0 = 0; r1 = INT_MAX; }
+    if (n > 0) {
+      Span& s = out[n - 1];
+      if (s.src == src && s.k1 == k0 && s.r0 == r0 && s.r1 == r1) {
+        s.k1 = k1;
+        return;
+      }
+    }
+    if (n < cap) {
+      Span s;
+      s.src = src; s.k0 = k0; s.k1 = k1; s.r0 = r0; s.r1 = r1; s.full = full;
+      s.pad0 = 0; s.pad1 = 0;
+      out[n++] = s;
+    }
+  }
+};
+
+// History-video tile c (canonical, oldest frame first) -> ring slot space.
+__device__ void emit_ring_tile(SpanWriter& w, const PlanParams& p, int c) {
+  const int a = c * TILE;
+  const int b = min(a + TILE, p.ring_tokens);
+  if (b <= a) return;
+  const int len = b - a;
+  const int s0 = (a + p.ring_rot) % p.ring_tokens;
+  if (s0 + len <= p.ring_tokens) {
+    w.emit(SRC_RING, s0, s0 + len, 0, INT_MAX);
+  } else {
+    w.emit(SRC_RING, s0, p.ring_tokens, 0, INT_MAX);
+    w.emit(SRC_RING, 0, s0 + len - p.ring_tokens, 0, INT_MAX);
+  }
+}
+
+__device__ int build_spans(const PlanParams& p, int qt, Span* out) {
+  SpanWriter w;
+  w.out = out;
+  w.n = 0;
+  w.cap = p.max_spans;
+  w.R0 = qt * p.tile_q;
+  w.R1 = min(w.R0 + p.tile_q, p.lq);
+
+  int c_begin = 0, c_end = 0;
+  if (p.sparse) {
+    c_begin = p.row_ptr[qt];
+    c_end = p.row_ptr[qt + 1];
+  }
+  const int n_video_tiles = p.n_hist_tiles + p.n_own_tiles;
+
+  // earlier segments' description heads: always visible
+  w.emit(SRC_HEADS, 0, p.head_tokens, 0, INT_MAX);
+  // history video still in the window
+  if (!p.sparse) {
+    w.emit(SRC_RING, 0, p.ring_tokens, 0, INT_MAX);
+  } else {
+    int last = -1;
+    for (int i = c_begin; i < c_end; ++i) {
+      const int c = p.col[i];
+      if (c <= last || c >= n_video_tiles) continue;
+      last = c;
+      if (c < p.n_hist_tiles) emit_ring_tile(w, p, c);
+    }
+  }
+  // own description head: always visible
+  w.emit(SRC_TXT, 0, p.head_len, 0, INT_MAX);
+  // own action tails: rows whose latent frame is inside [f0, f1)
+  for (int j = 0; j < p.m; ++j) {
+    const int off = p.tail_off[j];
+    w.emit(SRC_TXT, off, off + p.tail_len[j], p.tail_f0[j] * p.P, p.tail_f1[j] * p.P);
+  }
+  // own video: bidirectional inside the segment
+  if (!p.sparse) {
+    w.emit(SRC_VID, 0, p.lq, 0, INT_MAX);
+  } else {
+    int last = -1;
+    for (int i = c_begin; i < c_end; ++i) {
+      const int c = p.col[i];
+      if (c <= last || c >= n_video_tiles) continue;
+      last = c;
+      if (c >= p.n_hist_tiles) {
+        const int a = (c - p.n_hist_tiles) * TILE;
+        w.emit(SRC_VID, a, min(a + TILE, p.lq), 0, INT_MAX);
+      }
+    }
+  }
+  return w.n;
+}
+
+__global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
+  const int qt = blockIdx.x * 64 + threadIdx.x;
+  if (qt >= p.n_qtiles) return;
+  counts[qt] = build_spans(p, qt, spans + (int64_t)qt * p.max_spans);
+}
+
+// Canonical column of key k of a source (see hn.h, DENSE mode).
+__device__ int64_t canon_col(const DenseParams& d, int src, int k) {
+  const PlanParams& p = d.plan;
+  switch (src) {
+    case SRC_HEADS:
+      return k;
+    case SRC_RING: {
+      const int slot = k / p.P;
+      const int pp = k - slot * p.P;
+      const int oldest = p.ring_rot / p.P;
+      const int i = (slot - oldest + d.W) % d.W;
+      return (int64_t)p.head_tokens + (int64_t)i * p.P + pp;
+    }
+    case SRC_TXT:
+      return (int64_t)p.head_tokens + p.ring_tokens + k;
+    default:
+      return (int64_t)p.head_tokens + p.ring_tokens + p.text_len + k;
+  }
+}
+
+__global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
+  extern __shared__ Span sh_spans[];
+  __shared__ int sh_n;
+  const int row = d.row0 + blockIdx.x;
+  uint8_t* out = d.out + (int64_t)blockIdx.x * d.lk;
+  for (int64_t c = threadIdx.x; c < d.lk; c += blockDim.x) out[c] = 0;
+  if (threadIdx.x == 0) sh_n = build_spans(d.plan, row / d.plan.tile_q, sh_spans);
+  __syncthreads();
+  const int n = sh_n;
+  for (int e = 0; e < n; ++e) {
+    const Span s = sh_spans[e];
+    if (row < s.r0 || row >= s.r1) continue;
+    for (int k = s.k0 + threadIdx.x; k < s.k1; k += blockDim.x) out[canon_col(d, s.src, k)] = 1;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
+  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
+  Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) +
+                                        plan_counts_bytes(p.n_qtiles));
+  const int blocks = (p.n_qtiles + 63) / 64;
+  hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(64), 0, s, p, counts, spans);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense(const DenseParams& d, hipStream_t s) {
+  if (d.nrows == 0) return hipSuccess;
+  const size_t shmem = (size_t)d.plan.max_spans * sizeof(Span);
+  hipLaunchKernelGGL(dense_kernel, dim3(d.nrows), dim3(256), shmem, s, d);
+  return hipGetLastError();
+}
+
+}  // namespace hn

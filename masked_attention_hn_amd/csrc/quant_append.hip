@@ -1,0 +1,120 @@
+// INT8 quantize + ring append of one segment's keys and values (gfx950).
+//
+// Keys and values are stored INT8 with a float scale and computed in BF16
+// ("Hy-Nomas 拆解" teardown, section "单卡 4090 怎么做到的", first technique);
+// history video is a window of W latent frames, oldest evicted first (same
+// section, second technique).  Per (token, head) row of 128 values:
+//   scale = amax / 127 (IEEE fp32, correctly rounded),
+//   q     = round_half_even(x / scale) (correctly rounded fp32 quotient),
+//           clamped to [-127, 127]; a zero row stores scale 0 and q 0.
+//
+// The kernel is HBM-bound streaming: 16 lanes own one row (8 bf16 = 16 bytes
+// of K and 16 of V per lane), the row max is a 16-lane butterfly, and each lane
+// writes 8 int8 codes per tensor.  Consecutive 16-lane groups take the heads
+// of one token, so each wave reads 4 x 256 contiguous bytes per tensor.
+// The division is the compiler's correctly rounded fp32 divide (no fast-math);
+// fp32 denormals are preserved so subnormal scales quantize exactly.
+#include "hn_internal.h"
+
+namespace hn {
+namespace {
+
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Quantize the 8 values this lane holds; amax is the row maximum.
+__device__ inline uint2 quant8(const float (&x)[8], float scale, bool zero) {
+  uint32_t b[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float y = zero ? 0.0f : rintf(x[i] / scale);
+    y = fminf(fmaxf(y, -127.0f), 127.0f);
+    b[i] = (uint32_t)((int32_t)y) & 0xFFu;
+  }
+  uint2 r;
+  r.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
+  r.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
+  return r;
+}
+
+__device__ inline float row_amax16(float m) {
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  m = fmaxf(m, __shfl_xor(m, 8));
+  return m;
+}
+
+__device__ inline void unpack8(uint4 w, float (&x)[8], float& amax) {
+  x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
+  x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+  x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z);
+  x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(x[i]));
+  amax = m;
+}
+
+__global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
+  const int lane16 = threadIdx.x & 15;
+  const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int64_t rows = (int64_t)p.head_len + p.n_vid;
+  // Whole 16-lane groups leave together, so the butterflies below stay inside
+  // active lanes.
+  if (unit >= rows * p.H) return;
+  const int t = (int)(unit / p.H);
+  const int h = (int)(unit - (int64_t)t * p.H);
+
+  const __bf16 *ks, *vs;
+  int8_t *kd, *vd;
+  float *kds, *vds;
+  int64_t src_row, dst_row;
+  if (t < p.head_len) {
+    src_row = t;
+    dst_row = (int64_t)h * p.head_cap + p.head_pos + t;
+    ks = p.k_txt; vs = p.v_txt;
+    kd = p.heads_k; vd = p.heads_v; kds = p.heads_ks; vds = p.heads_vs;
+  } else {
+    const int r = p.vid_first + (t - p.head_len);
+    const int f = r / p.P;
+    const int pp = r - f * p.P;
+    const int slot = (int)((p.frames_seen + f) % p.W);
+    src_row = r;
+    dst_row = (int64_t)h * p.ring_cap + (int64_t)slot * p.P + pp;
+    ks = p.k_vid; vs = p.v_vid;
+    kd = p.ring_k; vd = p.ring_v; kds = p.ring_ks; vds = p.ring_vs;
+  }
+  const int64_t src = (src_row * p.H + h) * D + lane16 * 8;
+  const uint4 kw = *reinterpret_cast<const uint4*>(ks + src);
+  const uint4 vw = *reinterpret_cast<const uint4*>(vs + src);
+
+  float kx[8], vx[8], ka, va;
+  unpack8(kw, kx, ka);
+  unpack8(vw, vx, va);
+  ka = row_amax16(ka);
+  va = row_amax16(va);
+  const float ksc = ka / 127.0f;
+  const float vsc = va / 127.0f;
+  const uint2 kq = quant8(kx, ksc, ka == 0.0f);
+  const uint2 vq = quant8(vx, vsc, va == 0.0f);
+
+  *reinterpret_cast<uint2*>(kd + dst_row * D + lane16 * 8) = kq;
+  *reinterpret_cast<uint2*>(vd + dst_row * D + lane16 * 8) = vq;
+  if (lane16 == 0) {
+    kds[dst_row] = ka == 0.0f ? 0.0f : ksc;
+    vds[dst_row] = va == 0.0f ? 0.0f : vsc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quant_append(const AppendParams& p, hipStream_t s) {
+  const int64_t units = ((int64_t)p.head_len + p.n_vid) * p.H;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + 15) / 16;
+  hipLaunchKernelGGL(quant_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace hn

@@ -1,0 +1,89 @@
+"""Helpers that drive the HIP library through its C ABI for the GPU tests."""
+import numpy as np
+import torch
+
+import masked_attention_hn_amd as hn
+import oracle
+import workloads as W
+
+
+def dev(bits: np.ndarray) -> torch.Tensor:
+    """uint16 bf16 bit patterns -> bf16 tensor on the GPU."""
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def layout(index: int, seg: W.Segment) -> hn.SegLayout:
+    return hn.SegLayout(index, seg.frames, seg.tokens_per_frame, seg.head_len,
+                        seg.action_len, seg.action_f0, seg.action_f1)
+
+
+def new_cache(w: W.Workload) -> hn.KVCache:
+    return hn.KVCache(w.heads, w.current.tokens_per_frame, w.ring_frames, w.head_cap)
+
+
+def fill_history(w: W.Workload, data: dict, cache: hn.KVCache):
+    for s in range(w.query_segment):
+        d = data["segments"][s]
+        hn.hn_kv_quant_append(cache, layout(s, w.segments[s]), dev(d["k_txt"]), dev(d["v_txt"]),
+                              dev(d["k_vid"]), dev(d["v_vid"]))
+
+
+def sparse_of(w: W.Workload, data: dict):
+    if w.sparse_keep is None:
+        return None
+    csr = data["csr"]
+    return hn.BlockSparse(torch.from_numpy(csr["row_ptr"]), torch.from_numpy(csr["col"]),
+                          csr["n_qtiles"])
+
+
+class Run:
+    """Cache filled with the history of a workload, a plan for the query segment,
+    and the query segment's inputs on the GPU."""
+
+    def __init__(self, w: W.Workload, data: dict, use_sparse: bool = True):
+        self.w = w
+        self.data = data
+        self.cache = new_cache(w)
+        fill_history(w, data, self.cache)
+        S = w.query_segment
+        self.seg = layout(S, w.current)
+        d = data["segments"][S]
+        self.k_txt, self.v_txt = dev(d["k_txt"]), dev(d["v_txt"])
+        self.k_vid, self.v_vid = dev(d["k_vid"]), dev(d["v_vid"])
+        self.q = dev(data["q_vid"])
+        self.sparse = sparse_of(w, data) if use_sparse else None
+        self.plan = hn.build_plan(self.cache, self.seg, self.sparse)
+
+    def attn(self, with_lse=True):
+        out = hn.seg_attn(self.cache, self.seg, self.plan, self.q, self.k_txt, self.v_txt,
+                          self.k_vid, self.v_vid, with_lse=with_lse)
+        torch.cuda.synchronize()
+        return out
+
+    def dense(self, row0=0, nrows=None):
+        m = hn.dense_mask(self.cache, self.seg, self.sparse, row0, nrows)
+        torch.cuda.synchronize()
+        return m.cpu().numpy().astype(bool)
+
+
+def canonical_columns(w: W.Workload) -> np.ndarray:
+    """Full-sequence indices of the keys present in the cache state plus the
+    query segment, in the library's canonical DENSE order."""
+    tab = oracle.token_table(w)
+    S = w.query_segment
+    g0 = sum(s.frames for s in w.segments[:S])
+    seg, kind, gframe = tab["seg"], tab["kind"], tab["gframe"]
+    heads = np.nonzero((seg < S) & (kind == oracle.HEAD))[0]
+    vid = (seg < S) & (kind == oracle.VIDEO)
+    if w.window is not None:
+        vid &= gframe >= g0 - w.window
+    own = np.nonzero(seg == S)[0]
+    return np.concatenate([heads, np.nonzero(vid)[0], own])
+
+
+def sample_rows(nq: int, n: int, seed: int = 0) -> np.ndarray:
+    """Rows spread over every query tile, both ends and tile edges included."""
+    rng = np.random.default_rng(seed)
+    fixed = [0, 1, 127, 128, nq // 2, nq - 2, nq - 1]
+    extra = rng.choice(nq, size=max(0, min(n, nq) - len(fixed)), replace=False)
+    return np.unique(np.clip(np.concatenate([fixed, extra]), 0, nq - 1))

@@ -1,0 +1,138 @@
+"""Host-side checks of the C ABI that need no GPU: every function declared in
+include/hn.h is exported by libhn.so, and argument validation returns its
+status before anything is enqueued (device pointers below are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+import masked_attention_hn_amd as hn  # noqa: E402  (conftest builds the library if needed)
+
+FAKE = 0x10000  # a non-NULL device address; validation never dereferences it
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "hn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(hn_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert "hn_seg_attn_fwd" in names and "hn_kv_quant_append" in names
+    lib = ctypes.CDLL(hn.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(hn.EXPORTS) == set(names)
+
+
+def fake_cache(H=2, P=24, W=4, cap=48, head_dim=128):
+    return hn.hn_kv_cache(H, head_dim, P, W, cap, 0, *([FAKE] * 8), 0, 0, 0)
+
+
+def seg_c(index=0, F=2, P=24, h=16, tails=((8, 0, 1), (8, 1, 2))):
+    return hn.SegLayout(index, F, P, h, [t[0] for t in tails], [t[1] for t in tails],
+                        [t[2] for t in tails])
+
+
+def call_append(cache, seg):
+    return hn._lib.hn_kv_quant_append(ctypes.byref(cache), ctypes.byref(seg.c), FAKE, FAKE, FAKE,
+                                      FAKE, None)
+
+
+def test_status_strings():
+    assert hn.hn_status_string(0) == "ok"
+    assert "order" in hn.hn_status_string(hn.HN_ERR_ORDER)
+
+
+def test_append_validation():
+    c = fake_cache()
+    assert hn._lib.hn_kv_quant_append(None, ctypes.byref(seg_c().c), FAKE, FAKE, FAKE, FAKE,
+                                      None) == hn.HN_ERR_NULL
+    assert call_append(fake_cache(head_dim=64), seg_c()) == hn.HN_ERR_UNSUPPORTED
+    assert call_append(c, seg_c(index=1)) == hn.HN_ERR_ORDER
+    assert "segment index 1" in hn.hn_last_error()
+    assert call_append(c, seg_c(P=25)) == hn.HN_ERR_INVALID
+    assert call_append(c, seg_c(tails=((8, 1, 3),))) == hn.HN_ERR_INVALID      # window past F
+    assert call_append(c, seg_c(tails=((8, 2, 1),))) == hn.HN_ERR_INVALID      # f0 > f1
+    assert call_append(c, seg_c(tails=((-1, 0, 1),))) == hn.HN_ERR_INVALID
+    assert call_append(c, seg_c(tails=((1, 0, 1),) * 65)) == hn.HN_ERR_UNSUPPORTED
+    assert call_append(fake_cache(cap=10), seg_c()) == hn.HN_ERR_CAPACITY
+    c.head_tokens = 40
+    assert call_append(c, seg_c()) == hn.HN_ERR_CAPACITY
+    assert (c.frames_seen, c.head_tokens, c.segments) == (0, 40, 0)   # unchanged
+    z = fake_cache()
+    z.ring_k = None
+    assert call_append(z, seg_c()) == hn.HN_ERR_NULL
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device failure path")
+def test_failed_launch_leaves_cache_unchanged():
+    c = fake_cache()
+    st = call_append(c, seg_c())
+    assert st == hn.HN_ERR_HIP
+    assert (c.frames_seen, c.head_tokens, c.segments) == (0, 0, 0)
+
+
+def test_workspace_sizes_and_plan_checks():
+    c = fake_cache()
+    s = seg_c()
+    n = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    # counts padded to 256 bytes + one query tile x (4 + 2 tails) spans of 32 bytes
+    assert n == 256 + 1 * 6 * 32
+    bad = hn.hn_block_sparse(64, 64, 1, 0, FAKE, FAKE)
+    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad)) == 0
+    sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
+    n_sp = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(sp))
+    assert n_sp == 256 + (4 + 2 + 0 + 1 + 1) * 32
+    plan = hn.hn_tile_plan()
+    build = hn._lib.hn_attn_mask_build
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n - 1,
+                 ctypes.byref(plan), None) == hn.HN_ERR_WORKSPACE
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE + 4, n,
+                 ctypes.byref(plan), None) == hn.HN_ERR_INVALID                # misaligned
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n, None,
+                 None) == hn.HN_ERR_NULL
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * 1000,
+                 ctypes.byref(plan), None) == hn.HN_ERR_INVALID                # plan in DENSE
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 40, 9, FAKE, 10 ** 6, None,
+                 None) == hn.HN_ERR_INVALID                                    # rows past F*P
+    lk = 0 + 0 + 32 + 48
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * lk - 1, None,
+                 None) == hn.HN_ERR_WORKSPACE
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 7, 0, 0, FAKE, n,
+                 None, None) == hn.HN_ERR_INVALID
+
+
+def test_attention_rejects_stale_plan():
+    c = fake_cache()
+    s = seg_c()
+    plan = hn.hn_tile_plan(FAKE, 128, 1, 6, 0, 0, 0, 0, -1)
+    fwd = hn._lib.hn_seg_attn_fwd
+    args = [FAKE] * 6  # q, k_txt, v_txt, k_vid, v_vid, o
+    plan.frames_seen = 24          # built for another cache state
+    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None, 0.1,
+               None) == hn.HN_ERR_ORDER
+    plan.frames_seen = 0
+    plan.seg_index = 1
+    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None, 0.1,
+               None) == hn.HN_ERR_ORDER
+    plan.seg_index = 0
+    assert fwd(ctypes.byref(c), ctypes.byref(s.c), None, *args, None, 0.1, None) == hn.HN_ERR_NULL
+    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None,
+               float("nan"), None) == hn.HN_ERR_INVALID
+    s2 = seg_c(index=1)
+    assert fwd(ctypes.byref(c), ctypes.byref(s2.c), ctypes.byref(plan), *args, None, 0.1,
+               None) == hn.HN_ERR_ORDER
+
+
+def test_cache_sizes():
+    rb, rsb, hb, hsb = hn.hn_kv_cache_sizes(16, 18, 880, 2304)
+    assert rb == 16 * 18 * 880 * 128 and rsb == 16 * 18 * 880 * 4
+    assert hb == 16 * 2304 * 128 and hsb == 16 * 2304 * 4
+    with pytest.raises(hn.HNError):
+        hn.hn_kv_cache_sizes(0, 18, 880, 0)

@@ -1,0 +1,132 @@
+"""GPU parity of hn_seg_attn_fwd against the fp64 oracle.
+
+Bar on unit-variance normal inputs: max-abs error <= 2e-2 and mean-abs error
+<= 2e-3 (both sides use the same INT8 history, so the tolerance covers bf16
+rounding of the probabilities, the accumulation order and the bf16 output).
+Heavy-tailed (Student-t) keys and values concentrate some rows on a few keys,
+and |O| then reaches 5-20: the bf16 output alone is off by up to 2^-8 |O| and
+the bf16 probabilities by about 2^-9 |O|, which no bf16-output kernel can keep
+under 2e-2 once |O| >= 8.  Heavy-tailed cases are therefore held to
+|err| <= 2e-2 + 2^-7 |O_ref| elementwise, with the same mean-abs bar.
+Small layouts are compared on every row; the full-size target shapes on rows
+sampled across every tile, computed by the oracle against all keys.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import masked_attention_hn_amd as hn
+    import _gpu as G
+
+MAX_ABS = 2e-2
+MEAN_ABS = 2e-3
+_DATA = {}
+
+
+def data_of(name):
+    if name not in _DATA:
+        _DATA[name] = W.generate(W.config(name))
+    return _DATA[name]
+
+
+NORMAL = ("c1", "c1_evict", "c1_future", "c2", "c3", "c5", "c3_h2", "m1", "m3", "m4")
+
+
+def _compare(w, d, run, rows):
+    o, lse = run.attn()
+    o = o.float().cpu().numpy()[rows]
+    lse = lse.cpu().numpy()[:, rows]
+    ref, ref_lse, _ = oracle.attention(w, d, rows)
+    err = np.abs(o - ref)
+    i = np.unravel_index(np.argmax(err), err.shape)
+    print(f"  max-abs {err.max():.3e} (|O_ref| there {abs(ref[i]):.3f}, row {rows[i[0]]}) "
+          f"mean-abs {err.mean():.3e} lse max-abs {np.abs(lse - ref_lse).max():.3e}", flush=True)
+    if w.name in NORMAL:
+        assert w.kv_dist == "normal"
+        assert err.max() <= MAX_ABS
+    else:
+        assert np.all(err <= MAX_ABS + 2.0 ** -7 * np.abs(ref))
+    assert err.mean() <= MEAN_ABS
+    assert np.abs(lse - ref_lse).max() <= 1e-2
+    assert np.all(np.isfinite(o))
+
+
+@pytest.mark.parametrize("name", ["c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4"])
+def test_attention_small_all_rows(name):
+    print(f"[attn] {name}", flush=True)
+    w = W.config(name)
+    d = data_of(name)
+    run = G.Run(w, d)
+    _compare(w, d, run, np.arange(w.current.video_len))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c5", "c3_h2", "c4"])
+def test_attention_full_size_sampled_rows(name):
+    print(f"[attn] {name}", flush=True)
+    w = W.config(name)
+    d = data_of(name)
+    run = G.Run(w, d)
+    rows = G.sample_rows(w.current.video_len, 160 if name == "c4" else 256, seed=2)
+    _compare(w, d, run, rows)
+    if name == "c4":
+        _DATA.pop(name)
+
+
+def test_deterministic_bitwise():
+    w = W.config("m2")
+    d = data_of("m2")
+    run = G.Run(w, d)
+    o1, l1 = run.attn()
+    o2, l2 = run.attn()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(l1, l2)
+
+
+def test_invisible_keys_bitwise_on_gpu():
+    # own tail outside its window and unkept sparse tiles: perturbing them
+    # must leave every output bit unchanged
+    w = W.config("m4")
+    d = data_of("m4")
+    run = G.Run(w, d)
+    o1, _ = run.attn()
+    # tail 1 (3 tokens, window [6,7)) is invisible to rows of frames 0..5
+    k_txt = run.k_txt.clone()
+    v_txt = run.v_txt.clone()
+    tail1 = slice(19 + 200, 19 + 203)
+    run.k_txt[tail1] = torch.randn_like(run.k_txt[tail1]) * 4
+    run.v_txt[tail1] = torch.randn_like(run.v_txt[tail1]) * 4
+    o2, _ = run.attn()
+    P = w.current.tokens_per_frame
+    assert torch.equal(o1[:6 * P].view(torch.int16), o2[:6 * P].view(torch.int16))
+    assert not torch.equal(o1[6 * P:].view(torch.int16), o2[6 * P:].view(torch.int16))
+    run.k_txt.copy_(k_txt)
+    run.v_txt.copy_(v_txt)
+    # an own-video tile that query tile 0 does not keep
+    csr = d["csr"]
+    kept = set(csr["col"][csr["row_ptr"][0]:csr["row_ptr"][1]].tolist())
+    t = [c for c in range(csr["n_qtiles"]) if c not in kept][0]
+    run.k_vid[t * 128:(t + 1) * 128] *= 3
+    o3, _ = run.attn()
+    assert torch.equal(o1[:128].view(torch.int16), o3[:128].view(torch.int16))
+
+
+def test_zero_queries_mean_of_values():
+    # Q = 0: every visible key gets the same weight, O = mean of visible V
+    w = W.config("m1")
+    d = data_of("m1")
+    d0 = dict(d)
+    d0["q_vid"] = np.zeros_like(d["q_vid"])
+    run = G.Run(w, d0)
+    o, lse = run.attn()
+    ref, ref_lse, _ = oracle.attention(w, d0)
+    assert np.abs(o.float().cpu().numpy() - ref).max() < 1e-2
+    n_vis = oracle.mask(w).sum(axis=1)
+    assert np.abs(lse.cpu().numpy()[0] - np.log(n_vis)).max() < 1e-4

@@ -122,7 +122,7 @@ def config(name: str) -> Workload:
         s = [_seg(2, 24, 16, [8, 8], [(0, 1), (1, 2)]) for _ in range(3)]
         return Workload("c1_future", 2, s, 1, 4, 42)
     if name == "c2":
-        return Workload("c2", 16, [_seg(30, 390, 768, [128] * 4)], 0, 18, 1)
+        return Workload("c2", 16, [_seg(30, 390, 768, [128] * 4)], 0, None, 1)
     if name == "c3":
         s = [_seg(30, 880, 768, [128] * 4) for _ in range(4)]
         return Workload("c3", 16, s, 3, 18, 3)
@@ -131,7 +131,7 @@ def config(name: str) -> Workload:
         s.append(_seg(30, 880, 768, [128] * 4))
         return Workload("c4", 16, s, 6, None, 4, kv_dist="student_t4")
     if name == "c5":
-        return Workload("c5", 16, [_seg(30, 390, 768, [128] * 4)], 0, 18, 1,
+        return Workload("c5", 16, [_seg(30, 390, 768, [128] * 4)], 0, None, 1,
                         sparse_keep=0.25, sparse_seed=5)
     # per-GPU share of the 8-way head split at the steady-state shape
     if name == "c3_h2":
