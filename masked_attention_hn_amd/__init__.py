@@ -23,7 +23,8 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libhn.so")
+# HN_LIB may point at another build of the same library (used to compare builds)
+LIB_PATH = os.environ.get("HN_LIB") or os.path.join(_PKG, "libhn.so")
 
 HEAD_DIM = 128
 MAX_ACTIONS = 64

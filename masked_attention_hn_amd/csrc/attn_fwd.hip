@@ -9,17 +9,26 @@
 //   block  = one (head, 128-row query tile); 4 waves x 32 query rows.
 //   tile   = 64 keys of one span of the tile plan, staged in LDS as bf16:
 //            K as [key][d] (row pitch 136 elements) and V transposed as
-//            [d][key] (row pitch 72 elements, 16-byte groups XOR-swizzled by d/8).
+//            [d][key] (row pitch 72 elements).  The transposed writes are
+//            conflict-free because the 16 lanes that write together hold 16
+//            different 4-key groups of the same 8 d values.
 //            INT8 tiles are read from HBM as int8 (half the bytes), converted
 //            to bf16 in registers on their way into LDS (int8 -> bf16 is exact),
 //            and their fp32 scales are applied after the MFMA: the key scale to
 //            the score column, the value scale to the probability.
 //   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then holds
-//            16 keys of one query, so the row max/sum are in-lane plus one
-//            exchange with lane^32); online softmax in the log2 domain; the
+//            32 keys of one query, so the row max/sum are in-lane plus one
+//            v_permlane32_swap with lane^32); online softmax in the log2
+//            domain with the score scale folded into the exp2 argument; the
 //            probabilities are packed to bf16 in registers and used directly
 //            as the B operand of O^T = V^T P^T, whose accumulator keeps each
 //            query's 128 outputs in its own lane pair.
+//   rescale= lazy: the running max only moves (and O, l are rescaled) when a
+//            row's tile max exceeds it by more than 8 in log2 units, so
+//            probabilities stay <= 2^8 and the rescale is rare after the
+//            first tiles.  The result is exact algebra (same max in O and l).
+//   masks  = only partial tiles pay for masking: ragged tile ends and action
+//            tails whose row range does not cover all of a wave's rows.
 //   order  = the plan's span order, 64 keys at a time, double-buffered: global
 //            loads of tile n+1 are in flight while tile n is computed.
 //   grid   = XCD-aware: block b runs on XCD b % 8, and each XCD gets a
@@ -40,6 +49,7 @@ constexpr int QT = 32 * NW;           // query rows per block
 constexpr int KT = 64;                // keys per tile
 constexpr int KP = D + 8;             // LDS pitch of a K row (bf16 elements)
 constexpr int VP = KT + 8;            // LDS pitch of a V^T row (bf16 elements)
+constexpr float RESCALE_SLACK = 8.0f; // log2 units the running max may lag
 static_assert(QT == HN_TILE, "block rows must equal the plan tile");
 
 struct Smem {
@@ -58,13 +68,13 @@ struct TileDesc {
 __device__ inline int vt_pos(int key) {
   return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 }
-// XOR swizzle of 8-key groups by d/8 against LDS bank conflicts.
-__device__ inline int vt_index(int d, int pos) { return d * VP + (pos ^ (((d >> 3) & 7) << 3)); }
+__device__ inline int vt_index(int d, int pos) { return d * VP + pos; }
 
-__device__ inline uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) {
-  return __builtin_amdgcn_perm(b, a, sel);
-}
-// Low halves of a and b -> (a.lo | b.lo << 16); high halves -> (a.hi | b.hi << 16).
+// Thread -> (4-key group, 8-d chunk) of the V transpose: the 16 lanes of a
+// quarter-wave share the d chunk and cover all 16 key groups.
+__device__ inline int v_kq(int tid) { return tid & 15; }
+__device__ inline int v_dc(int tid) { return tid >> 4; }
+
 __device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
@@ -73,6 +83,16 @@ __device__ inline uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
   const float f0 = (float)(int8_t)((w >> (8 * byte0)) & 0xFF);
   const float f1 = (float)(int8_t)((w >> (8 * byte0 + 8)) & 0xFF);
   return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
+}
+
+// max / sum of a value and its lane^32 partner
+__device__ inline float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct Prefetch {
@@ -90,30 +110,26 @@ __device__ inline const float* sc_base(const AttnParams& p, int src, bool is_v, 
   return (is_v ? p.ring_vs : p.ring_ks) + (int64_t)h * p.ring_cap;
 }
 
-// Global -> registers for one tile.  Rows at or past nk read as zero.
+// Global -> registers for one tile.  Keys at or past nk re-read key nk-1 (always
+// a valid row); the math masks their scores, so their probabilities are 0.
 __device__ inline void load_tile(const AttnParams& p, const TileDesc& t, int h, Prefetch& pf) {
   const int tid = threadIdx.x;
-  const uint4 z = make_uint4(0, 0, 0, 0);
+  const int last = t.nk - 1;
+  const int kq = v_kq(tid), dc = v_dc(tid);
   if (t.src >= SRC_TXT) {
-    const __bf16* kbase = (t.src == SRC_TXT) ? p.k_txt : p.k_vid;
-    const __bf16* vbase = (t.src == SRC_TXT) ? p.v_txt : p.v_vid;
+    const __bf16* kbase = ((t.src == SRC_TXT) ? p.k_txt : p.k_vid) + (int64_t)t.kb * p.H * D + h * D;
+    const __bf16* vbase = ((t.src == SRC_TXT) ? p.v_txt : p.v_vid) + (int64_t)t.kb * p.H * D + h * D;
     const int64_t rs = (int64_t)p.H * D;  // token stride
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int id = c * 256 + tid;
-      const int key = id >> 4, dch = id & 15;
-      pf.k[c] = key < t.nk
-                    ? *reinterpret_cast<const uint4*>(kbase + (int64_t)(t.kb + key) * rs + h * D + dch * 8)
-                    : z;
+      const int key = min(id >> 4, last), dch = id & 15;
+      pf.k[c] = *reinterpret_cast<const uint4*>(kbase + key * rs + dch * 8);
     }
-    const int lane = tid & 63, wave = tid >> 6;
-    const int kq = (lane & 3) + 4 * wave, dc = lane >> 2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = 4 * kq + r;
-      pf.v[r] = key < t.nk
-                    ? *reinterpret_cast<const uint4*>(vbase + (int64_t)(t.kb + key) * rs + h * D + dc * 8)
-                    : z;
+      const int key = min(4 * kq + r, last);
+      pf.v[r] = *reinterpret_cast<const uint4*>(vbase + key * rs + dc * 8);
     }
     pf.sc = 1.0f;
   } else {
@@ -122,35 +138,30 @@ __device__ inline void load_tile(const AttnParams& p, const TileDesc& t, int h, 
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       const int id = c * 256 + tid;
-      const int key = id >> 3, dch = id & 7;
-      pf.k[c] = key < t.nk ? *reinterpret_cast<const uint4*>(kbase + key * D + dch * 16) : z;
+      const int key = min(id >> 3, last), dch = id & 7;
+      pf.k[c] = *reinterpret_cast<const uint4*>(kbase + key * D + dch * 16);
     }
-    const int lane = tid & 63, wave = tid >> 6;
-    const int kq = (lane & 3) + 4 * wave, dc = lane >> 2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int key = 4 * kq + r;
-      uint2 w = make_uint2(0, 0);
-      if (key < t.nk) w = *reinterpret_cast<const uint2*>(vbase + key * D + dc * 8);
+      const int key = min(4 * kq + r, last);
+      const uint2 w = *reinterpret_cast<const uint2*>(vbase + key * D + dc * 8);
       pf.v[r] = make_uint4(w.x, w.y, 0, 0);
     }
     float sc = 0.0f;
     if (tid < 2 * KT) {
-      const int key = tid & (KT - 1);
-      const float* sb = sc_base(p, t.src, tid >= KT, h);
-      sc = key < t.nk ? sb[t.kb + key] : 0.0f;
+      const int key = min(tid & (KT - 1), last);
+      sc = sc_base(p, t.src, tid >= KT, h)[t.kb + key];
     }
     pf.sc = sc;
   }
 }
 
 // Registers -> LDS buffer `b` (bf16 K rows, bf16 V^T rows, scales).
-__device__ inline void store_tile(Smem& sm, int b, const TileDesc& t, const Prefetch& pf) {
+__device__ inline void store_tile(Smem& sm, int b, bool i8, const Prefetch& pf) {
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int kq = (lane & 3) + 4 * wave, dc = lane >> 2;
+  const int kq = v_kq(tid), dc = v_dc(tid);
   uint32_t rows[4][4];  // V rows as 4 x (8 bf16) packed words
-  if (t.src >= SRC_TXT) {
+  if (!i8) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int id = c * 256 + tid;
@@ -198,13 +209,125 @@ __device__ inline void store_tile(Smem& sm, int b, const TileDesc& t, const Pref
   }
 }
 
-__device__ inline bf16x8 lds8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ inline bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 __device__ inline bf16x8 pack_p(const float* x) {
   bf16x8 r;
 #pragma unroll
   for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
   return r;
+}
+
+struct RowState {
+  float m;   // running max (log2 units) of this lane's query
+  float l;   // this lane's partial sum of probabilities (partner holds the rest)
+};
+
+// One 64-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
+//   I8   : the tile comes from the INT8 cache (per-key scales in LDS)
+//   MASK : some keys (ragged end) or rows (tail window) of the tile are invisible
+template <bool I8, bool MASK>
+__device__ __forceinline__ void tile_math(const Smem& sm, int buf, const bf16x8 (&qreg)[8],
+                                          f32x16 (&acc)[4], RowState& st, float scale_log2,
+                                          int nk, bool row_ok) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 5, l32 = lane & 31;
+  const __bf16* kl = sm.k[buf];
+  const __bf16* vl = sm.vt[buf];
+
+  f32x16 s[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 a = f32x16{};
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const bf16x8 kk = ld8(kl + (kb * 32 + l32) * KP + 16 * t + 8 * g);
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[t], a, 0, 0, 0);
+    }
+    s[kb] = a;
+  }
+
+  // scores in log2 units; element 4r+i of block kb is key kb*32 + 8r + 4g + i
+  float x[2][16];
+  float mx;
+  if (I8 || MASK) {
+    mx = -INFINITY;
+    const int nkg = row_ok ? nk - 4 * g : INT_MIN;  // key kb*32+8r+4g+i visible iff kb*32+8r+i < nkg
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float4 c4 = make_float4(scale_log2, scale_log2, scale_log2, scale_log2);
+        if (I8) {
+          const float4 ksc = *reinterpret_cast<const float4*>(&sm.ks[buf][kb * 32 + 8 * r + 4 * g]);
+          c4 = make_float4(ksc.x * scale_log2, ksc.y * scale_log2, ksc.z * scale_log2, ksc.w * scale_log2);
+        }
+        const float cc[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float v = s[kb][4 * r + i] * cc[i];
+          if (MASK && kb * 32 + 8 * r + i >= nkg) v = -INFINITY;
+          x[kb][4 * r + i] = v;
+          mx = fmaxf(mx, v);
+        }
+      }
+    }
+  } else {
+    // every key visible and one scale: take the max of the raw scores
+    float m0 = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s[kb][i]);
+    mx = m0 * scale_log2;
+  }
+  mx = pair_max(mx);
+
+  // lazy rescale: move the running max only when it lags by more than the slack
+  if (__any(mx > st.m + RESCALE_SLACK)) {
+    const float m_new = fmaxf(st.m, mx);
+    const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] *= alpha;
+  }
+  const float m_use = (st.m == -INFINITY) ? 0.0f : st.m;
+
+  float psum = 0.0f;
+  bf16x8 pb[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    float pv[16];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float4 vsc;
+      if (I8) vsc = *reinterpret_cast<const float4*>(&sm.vs[buf][kb * 32 + 8 * r + 4 * g]);
+      const float vv[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e2;
+        if (I8 || MASK) e2 = __builtin_amdgcn_exp2f(x[kb][4 * r + i] - m_use);
+        else e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][4 * r + i], scale_log2, -m_use));
+        psum += e2;
+        pv[4 * r + i] = I8 ? e2 * vv[i] : e2;
+      }
+    }
+    pb[2 * kb] = pack_p(pv);
+    pb[2 * kb + 1] = pack_p(pv + 8);
+  }
+  st.l += psum;
+
+  // O^T += V^T P^T
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int d = 32 * c + l32;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const bf16x8 vv = ld8(vl + vt_index(d, 16 * t + 8 * g));
+      acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[c], 0, 0, 0);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
@@ -227,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
     const __bf16* qrow = p.q + ((int64_t)(row_valid ? row : 0) * p.H + h) * D;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      bf16x8 v = lds8(qrow + 16 * t + 8 * g);
+      bf16x8 v = ld8(qrow + 16 * t + 8 * g);
       if (!row_valid) v = bf16x8{};
       qreg[t] = v;
     }
@@ -236,13 +359,14 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
   f32x16 acc[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) acc[c] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.0f;
+  RowState st;
+  st.m = -INFINITY;
+  st.l = 0.0f;
 
   const int n_spans = p.counts[qt];
   const Span* spans = p.spans + (int64_t)qt * p.max_spans;
 
-  // tile iterator over the spans
+  // tile iterator over the spans (block-uniform)
   int e = 0;
   int kpos = n_spans > 0 ? spans[0].k0 : 0;
   auto next_tile = [&](TileDesc& t) -> bool {
@@ -266,7 +390,7 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
   Prefetch pf;
   if (have) {
     load_tile(p, cur, h, pf);
-    store_tile(sm, 0, cur, pf);
+    store_tile(sm, 0, cur.src < SRC_TXT, pf);
   }
   __syncthreads();
   int buf = 0;
@@ -274,93 +398,23 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
     const bool have_next = next_tile(nxt);
     if (have_next) load_tile(p, nxt, h, pf);
 
-    // skip the math if no row of this wave can see the tile
+    // rows of this wave that see the tile; skip the math if none does
     const bool wave_live = (cur.r0 < wrow0 + 32) && (cur.r1 > wrow0);
     if (wave_live) {
+      const bool rows_all = (cur.r0 <= wrow0) && (cur.r1 >= wrow0 + 32);
       const bool row_ok = row >= cur.r0 && row < cur.r1;
-      const bool is_i8 = cur.src < SRC_TXT;
-      const __bf16* kl = sm.k[buf];
-      const __bf16* vl = sm.vt[buf];
-
-      // S^T for two 32-key blocks
-      f32x16 s[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 a = f32x16{};
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const bf16x8 kk = lds8(kl + (kb * 32 + l32) * KP + 16 * t + 8 * g);
-          a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[t], a, 0, 0, 0);
-        }
-        s[kb] = a;
-      }
-
-      // scale, mask, running max (log2 domain)
-      float x[2][16];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kbase = kb * 32 + 8 * r + 4 * g;
-          float4 ksc = make_float4(1.f, 1.f, 1.f, 1.f);
-          if (is_i8) ksc = *reinterpret_cast<const float4*>(&sm.ks[buf][kbase]);
-          const float kscl[4] = {ksc.x, ksc.y, ksc.z, ksc.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kbase + i;
-            float v = s[kb][4 * r + i] * (p.scale_log2 * kscl[i]);
-            if (key >= cur.nk || !row_ok) v = -INFINITY;
-            x[kb][4 * r + i] = v;
-            mx = fmaxf(mx, v);
-          }
-        }
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      m_run = m_new;
-
-      float psum = 0.0f;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float pv[16];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float4 vsc = make_float4(1.f, 1.f, 1.f, 1.f);
-          if (is_i8) vsc = *reinterpret_cast<const float4*>(&sm.vs[buf][kb * 32 + 8 * r + 4 * g]);
-          const float vscl[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e2 = __builtin_amdgcn_exp2f(x[kb][4 * r + i] - m_use);
-            psum += e2;
-            pv[4 * r + i] = e2 * vscl[i];
-          }
-        }
-        pb[2 * kb] = pack_p(pv);
-        pb[2 * kb + 1] = pack_p(pv + 8);
-      }
-      l_run = l_run * alpha + psum;
-
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[c] *= alpha;
-
-      // O^T += V^T P^T
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int d = 32 * c + l32;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int pos = 16 * t + 8 * g;
-          const bf16x8 vv = lds8(vl + vt_index(d, pos));
-          acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[t], acc[c], 0, 0, 0);
-        }
+      const bool mask = (cur.nk < KT) || !rows_all;
+      const float sl = p.scale_log2;
+      if (cur.src < SRC_TXT) {
+        if (mask) tile_math<true, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
+        else tile_math<true, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
+      } else {
+        if (mask) tile_math<false, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
+        else tile_math<false, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
       }
     }
 
-    if (have_next) store_tile(sm, buf ^ 1, nxt, pf);
+    if (have_next) store_tile(sm, buf ^ 1, nxt.src < SRC_TXT, pf);
     __syncthreads();
     cur = nxt;
     have = have_next;
@@ -368,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
   }
 
   // epilogue: O = acc / l, lse = (m + log2 l) * ln 2
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = pair_sum(st.l);
   const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
   if (row_valid) {
     __bf16* orow = p.o + ((int64_t)row * p.H + h) * D;
@@ -387,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
     }
     if (p.lse != nullptr && g == 0) {
       p.lse[(int64_t)h * p.lq + row] =
-          l_tot > 0.0f ? (m_run + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+          l_tot > 0.0f ? (st.m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
   }
 }
