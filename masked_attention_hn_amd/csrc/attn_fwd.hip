@@ -75,15 +75,6 @@ __device__ inline int vt_index(int d, int pos) { return d * VP + pos; }
 __device__ inline int v_kq(int tid) { return tid & 15; }
 __device__ inline int v_dc(int tid) { return tid >> 4; }
 
-__device__ inline uint32_t pack_lo(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
-__device__ inline uint32_t pack_hi(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-// int8 -> bf16 (exact for |q| <= 127): two signed bytes -> packed bf16 pair.
-__device__ inline uint32_t i8pair_to_bf16(uint32_t w, int byte0) {
-  const float f0 = (float)(int8_t)((w >> (8 * byte0)) & 0xFF);
-  const float f1 = (float)(int8_t)((w >> (8 * byte0 + 8)) & 0xFF);
-  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xFFFF0000u);
-}
 
 // max / sum of a value and its lane^32 partner
 __device__ inline float pair_max(float x) {
@@ -95,65 +86,109 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0.
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ inline uint4 ld_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ inline uint2 ld_b64(rsrc_t r, uint32_t voff, uint32_t soff) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
+}
+
+// Two signed bytes of w (bytes b, b+1) -> packed bf16 pair (exact for |q| <= 127).
+__device__ inline uint32_t i8x2_bf16(uint32_t w, int b) {
+  const bf16x2 v = {(__bf16)(float)(int8_t)(w >> (8 * b)), (__bf16)(float)(int8_t)(w >> (8 * b + 8))};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 struct Prefetch {
   uint4 k[4];
   uint4 v[4];
   float sc;
 };
 
-__device__ inline const int8_t* i8_base(const AttnParams& p, int src, bool is_v, int h) {
-  if (src == SRC_HEADS) return (is_v ? p.heads_v : p.heads_k) + (int64_t)h * p.head_cap * D;
-  return (is_v ? p.ring_v : p.ring_k) + (int64_t)h * p.ring_cap * D;
-}
-__device__ inline const float* sc_base(const AttnParams& p, int src, bool is_v, int h) {
-  if (src == SRC_HEADS) return (is_v ? p.heads_vs : p.heads_ks) + (int64_t)h * p.head_cap;
-  return (is_v ? p.ring_vs : p.ring_ks) + (int64_t)h * p.ring_cap;
+// Buffer resources of one head's key/value sources and the per-thread
+// offsets of its share of a tile (both fixed for the whole block).
+struct Sources {
+  rsrc_t k_txt, v_txt, k_vid, v_vid;                     // bf16, token-major
+  rsrc_t k_heads, v_heads, ks_heads, vs_heads;           // INT8 head store + scales
+  rsrc_t k_ring, v_ring, ks_ring, vs_ring;               // INT8 ring + scales
+  uint32_t tok_bytes;      // bf16 token stride = H * D * 2
+  uint32_t vo_kb, vo_vb;   // bf16 K / V thread offsets
+  uint32_t vo_ki, vo_vi;   // INT8 K / V thread offsets
+  uint32_t vo_sc;          // scale thread offset
+};
+
+__device__ inline void init_sources(const AttnParams& p, int h, Sources& S) {
+  const int tid = threadIdx.x;
+  const uint32_t tb = (uint32_t)p.H * D * 2;
+  S.tok_bytes = tb;
+  const uint32_t hoff = (uint32_t)h * D * 2;
+  const uint32_t txt_bytes = p.txt_len > 0 ? (uint32_t)p.txt_len * tb - hoff : 0u;
+  S.k_txt = make_rsrc(p.k_txt + h * D, txt_bytes);
+  S.v_txt = make_rsrc(p.v_txt + h * D, txt_bytes);
+  S.k_vid = make_rsrc(p.k_vid + h * D, (uint32_t)p.lq * tb - hoff);
+  S.v_vid = make_rsrc(p.v_vid + h * D, (uint32_t)p.lq * tb - hoff);
+  S.k_heads = make_rsrc(p.heads_k + (int64_t)h * p.head_cap * D, (uint32_t)p.head_cap * D);
+  S.v_heads = make_rsrc(p.heads_v + (int64_t)h * p.head_cap * D, (uint32_t)p.head_cap * D);
+  S.ks_heads = make_rsrc(p.heads_ks + (int64_t)h * p.head_cap, (uint32_t)p.head_cap * 4);
+  S.vs_heads = make_rsrc(p.heads_vs + (int64_t)h * p.head_cap, (uint32_t)p.head_cap * 4);
+  S.k_ring = make_rsrc(p.ring_k + (int64_t)h * p.ring_cap * D, (uint32_t)p.ring_cap * D);
+  S.v_ring = make_rsrc(p.ring_v + (int64_t)h * p.ring_cap * D, (uint32_t)p.ring_cap * D);
+  S.ks_ring = make_rsrc(p.ring_ks + (int64_t)h * p.ring_cap, (uint32_t)p.ring_cap * 4);
+  S.vs_ring = make_rsrc(p.ring_vs + (int64_t)h * p.ring_cap, (uint32_t)p.ring_cap * 4);
+  const int kq = v_kq(tid), dc = v_dc(tid);
+  S.vo_kb = (uint32_t)(tid >> 4) * tb + (tid & 15) * 16;   // key c*16 + tid/16, 16-byte chunk tid%16
+  S.vo_vb = (uint32_t)(4 * kq) * tb + dc * 16;             // key 4kq + r, d chunk dc
+  S.vo_ki = (uint32_t)(tid >> 3) * D + (tid & 7) * 16;     // key c*32 + tid/8, 16 codes
+  S.vo_vi = (uint32_t)(4 * kq) * D + dc * 8;               // key 4kq + r, 8 codes
+  S.vo_sc = (uint32_t)(tid & (KT - 1)) * 4;
 }
 
-// Global -> registers for one tile.  Keys at or past nk re-read key nk-1 (always
-// a valid row); the math masks their scores, so their probabilities are 0.
-__device__ inline void load_tile(const AttnParams& p, const TileDesc& t, int h, Prefetch& pf) {
+__device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb, Prefetch& pf) {
+  const uint32_t base = (uint32_t)kb * S.tok_bytes;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) pf.k[c] = ld_b128(rk, S.vo_kb, base + c * 16 * S.tok_bytes);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) pf.v[r] = ld_b128(rv, S.vo_vb, base + r * S.tok_bytes);
+  pf.sc = 1.0f;
+}
+
+__device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rks, rsrc_t rvs,
+                               int kb, int nk, Prefetch& pf) {
   const int tid = threadIdx.x;
-  const int last = t.nk - 1;
-  const int kq = v_kq(tid), dc = v_dc(tid);
-  if (t.src >= SRC_TXT) {
-    const __bf16* kbase = ((t.src == SRC_TXT) ? p.k_txt : p.k_vid) + (int64_t)t.kb * p.H * D + h * D;
-    const __bf16* vbase = ((t.src == SRC_TXT) ? p.v_txt : p.v_vid) + (int64_t)t.kb * p.H * D + h * D;
-    const int64_t rs = (int64_t)p.H * D;  // token stride
+  const uint32_t base = (uint32_t)kb * D;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int id = c * 256 + tid;
-      const int key = min(id >> 4, last), dch = id & 15;
-      pf.k[c] = *reinterpret_cast<const uint4*>(kbase + key * rs + dch * 8);
-    }
+  for (int c = 0; c < 2; ++c) pf.k[c] = ld_b128(rk, S.vo_ki, base + c * 32 * D);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = min(4 * kq + r, last);
-      pf.v[r] = *reinterpret_cast<const uint4*>(vbase + key * rs + dc * 8);
-    }
-    pf.sc = 1.0f;
-  } else {
-    const int8_t* kbase = i8_base(p, t.src, false, h) + (int64_t)t.kb * D;
-    const int8_t* vbase = i8_base(p, t.src, true, h) + (int64_t)t.kb * D;
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const int id = c * 256 + tid;
-      const int key = min(id >> 3, last), dch = id & 7;
-      pf.k[c] = *reinterpret_cast<const uint4*>(kbase + key * D + dch * 16);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = min(4 * kq + r, last);
-      const uint2 w = *reinterpret_cast<const uint2*>(vbase + key * D + dc * 8);
-      pf.v[r] = make_uint4(w.x, w.y, 0, 0);
-    }
-    float sc = 0.0f;
-    if (tid < 2 * KT) {
-      const int key = min(tid & (KT - 1), last);
-      sc = sc_base(p, t.src, tid >= KT, h)[t.kb + key];
-    }
-    pf.sc = sc;
+  for (int r = 0; r < 4; ++r) {
+    const uint2 w = ld_b64(rv, S.vo_vi, base + r * D);
+    pf.v[r] = make_uint4(w.x, w.y, 0, 0);
   }
+  float sc = 0.0f;
+  if (tid < 2 * KT) {
+    const float v = __uint_as_float(
+        __builtin_amdgcn_raw_buffer_load_b32(tid < KT ? rks : rvs, S.vo_sc, (uint32_t)kb * 4, 0));
+    sc = (tid & (KT - 1)) < nk ? v : 0.0f;
+  }
+  pf.sc = sc;
+}
+
+// Global -> registers for one tile.  Keys past the span end read other finite
+// data (or 0 past the buffer end) and are masked by the math; their value
+// scales are zeroed so that a 0 probability times the scale stays 0.
+__device__ inline void load_tile(const Sources& S, const TileDesc& t, Prefetch& pf) {
+  if (t.src == SRC_VID) load_bf16(S, S.k_vid, S.v_vid, t.kb, pf);
+  else if (t.src == SRC_TXT) load_bf16(S, S.k_txt, S.v_txt, t.kb, pf);
+  else if (t.src == SRC_RING) load_i8(S, S.k_ring, S.v_ring, S.ks_ring, S.vs_ring, t.kb, t.nk, pf);
+  else load_i8(S, S.k_heads, S.v_heads, S.ks_heads, S.vs_heads, t.kb, t.nk, pf);
 }
 
 // Registers -> LDS buffer `b` (bf16 K rows, bf16 V^T rows, scales).
@@ -164,8 +199,7 @@ __device__ inline void store_tile(Smem& sm, int b, bool i8, const Prefetch& pf) 
   if (!i8) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int id = c * 256 + tid;
-      const int key = id >> 4, dch = id & 15;
+      const int key = c * 16 + (tid >> 4), dch = tid & 15;
       *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 8]) = pf.k[c];
     }
 #pragma unroll
@@ -175,21 +209,20 @@ __device__ inline void store_tile(Smem& sm, int b, bool i8, const Prefetch& pf) 
   } else {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const int id = c * 256 + tid;
-      const int key = id >> 3, dch = id & 7;
+      const int key = c * 32 + (tid >> 3), dch = tid & 7;
       const uint4 w = pf.k[c];
       uint4 lo, hi;
-      lo.x = i8pair_to_bf16(w.x, 0); lo.y = i8pair_to_bf16(w.x, 2);
-      lo.z = i8pair_to_bf16(w.y, 0); lo.w = i8pair_to_bf16(w.y, 2);
-      hi.x = i8pair_to_bf16(w.z, 0); hi.y = i8pair_to_bf16(w.z, 2);
-      hi.z = i8pair_to_bf16(w.w, 0); hi.w = i8pair_to_bf16(w.w, 2);
+      lo.x = i8x2_bf16(w.x, 0); lo.y = i8x2_bf16(w.x, 2);
+      lo.z = i8x2_bf16(w.y, 0); lo.w = i8x2_bf16(w.y, 2);
+      hi.x = i8x2_bf16(w.z, 0); hi.y = i8x2_bf16(w.z, 2);
+      hi.z = i8x2_bf16(w.w, 0); hi.w = i8x2_bf16(w.w, 2);
       *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 16]) = lo;
       *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 16 + 8]) = hi;
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      rows[r][0] = i8pair_to_bf16(pf.v[r].x, 0); rows[r][1] = i8pair_to_bf16(pf.v[r].x, 2);
-      rows[r][2] = i8pair_to_bf16(pf.v[r].y, 0); rows[r][3] = i8pair_to_bf16(pf.v[r].y, 2);
+      rows[r][0] = i8x2_bf16(pf.v[r].x, 0); rows[r][1] = i8x2_bf16(pf.v[r].x, 2);
+      rows[r][2] = i8x2_bf16(pf.v[r].y, 0); rows[r][3] = i8x2_bf16(pf.v[r].y, 2);
     }
     if (tid < KT) sm.ks[b][tid] = pf.sc;
     else if (tid < 2 * KT) sm.vs[b][tid - KT] = pf.sc;
@@ -200,10 +233,10 @@ __device__ inline void store_tile(Smem& sm, int b, bool i8, const Prefetch& pf) 
   for (int w = 0; w < 4; ++w) {
     const int d0 = dc * 8 + 2 * w;
     uint2 e, o;
-    e.x = pack_lo(rows[0][w], rows[1][w]);
-    e.y = pack_lo(rows[2][w], rows[3][w]);
-    o.x = pack_hi(rows[0][w], rows[1][w]);
-    o.y = pack_hi(rows[2][w], rows[3][w]);
+    e.x = __builtin_amdgcn_perm(rows[1][w], rows[0][w], 0x05040100u);
+    e.y = __builtin_amdgcn_perm(rows[3][w], rows[2][w], 0x05040100u);
+    o.x = __builtin_amdgcn_perm(rows[1][w], rows[0][w], 0x07060302u);
+    o.y = __builtin_amdgcn_perm(rows[3][w], rows[2][w], 0x07060302u);
     *reinterpret_cast<uint2*>(&sm.vt[b][vt_index(d0, pos)]) = e;
     *reinterpret_cast<uint2*>(&sm.vt[b][vt_index(d0 + 1, pos)]) = o;
   }
@@ -344,17 +377,18 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
   const int row = wrow0 + l32;
   const bool row_valid = row < p.lq;
 
-  // Q^T as the B operand: lane (q, g) holds Q[q][16t + 8g .. +8] for t = 0..7
+  // Q^T as the B operand: lane (q, g) holds Q[q][16t + 8g .. +8] for t = 0..7;
+  // rows past the segment read as 0
   bf16x8 qreg[8];
   {
-    const __bf16* qrow = p.q + ((int64_t)(row_valid ? row : 0) * p.H + h) * D;
+    const uint32_t tb = (uint32_t)p.H * D * 2;
+    const rsrc_t rq = make_rsrc(p.q + h * D, (uint32_t)p.lq * tb - (uint32_t)h * D * 2);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      bf16x8 v = ld8(qrow + 16 * t + 8 * g);
-      if (!row_valid) v = bf16x8{};
-      qreg[t] = v;
-    }
+    for (int t = 0; t < 8; ++t)
+      qreg[t] = __builtin_bit_cast(bf16x8, ld_b128(rq, (uint32_t)row * tb + 16 * g, 32 * t));
   }
+  Sources S;
+  init_sources(p, h, S);
 
   f32x16 acc[4];
 #pragma unroll
@@ -389,14 +423,14 @@ __global__ __launch_bounds__(256, 2) void seg_attn_fwd_kernel(AttnParams p) {
   bool have = next_tile(cur);
   Prefetch pf;
   if (have) {
-    load_tile(p, cur, h, pf);
+    load_tile(S, cur, pf);
     store_tile(sm, 0, cur.src < SRC_TXT, pf);
   }
   __syncthreads();
   int buf = 0;
   while (have) {
     const bool have_next = next_tile(nxt);
-    if (have_next) load_tile(p, nxt, h, pf);
+    if (have_next) load_tile(S, nxt, pf);
 
     // rows of this wave that see the tile; skip the math if none does
     const bool wave_live = (cur.r0 < wrow0 + 32) && (cur.r1 > wrow0);

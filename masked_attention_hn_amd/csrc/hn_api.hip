@@ -302,6 +302,13 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
   if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
+  // the kernel addresses every source through 32-bit buffer offsets
+  const int64_t tok_bytes = (int64_t)c->num_heads * HN_HEAD_DIM * 2;
+  const int64_t lim = INT_MAX;
+  if ((int64_t)lq * tok_bytes > lim || tl * tok_bytes > lim ||
+      (int64_t)c->head_cap_tokens * HN_HEAD_DIM > lim ||
+      (int64_t)c->window_frames * P * HN_HEAD_DIM > lim)
+    return fail(HN_ERR_UNSUPPORTED, "a key/value source exceeds 2 GiB");
   hn::AttnParams p;
   std::memset(&p, 0, sizeof(p));
   p.H = c->num_heads;
@@ -313,6 +320,7 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.head_cap = c->head_cap_tokens;
   p.ring_cap = c->window_frames * P;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.txt_len = (int32_t)tl;
   p.counts = static_cast<const int32_t*>(plan->dev);
   p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
                                               hn::plan_counts_bytes(plan->n_qtiles));

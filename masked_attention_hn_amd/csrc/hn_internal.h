@@ -77,7 +77,7 @@ struct AttnParams {
   int32_t head_cap;      // head-store stride (tokens) per head
   int32_t ring_cap;      // ring stride (tokens) per head = W*P
   float scale_log2;      // sm_scale * log2(e)
-  int32_t pad0;
+  int32_t txt_len;       // h + sum(a) text rows of the current segment
   const int32_t* counts;
   const Span* spans;
   const __bf16* q;
