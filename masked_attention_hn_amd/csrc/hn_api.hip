@@ -90,8 +90,8 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   std::memset(pp, 0, sizeof(*pp));
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  pp->tile_q = HN_TILE;
-  pp->n_qtiles = (int)ceil_div(lq, HN_TILE);
+  pp->tile_q = sp ? HN_TILE : hn::attn_dense_rows();
+  pp->n_qtiles = (int)ceil_div(lq, pp->tile_q);
   pp->lq = lq;
   pp->P = P;
   pp->head_tokens = c->head_tokens;
@@ -111,7 +111,7 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     off += s->action_len[j];
   }
   pp->n_hist_tiles = (int)ceil_div(pp->ring_tokens, HN_TILE);
-  pp->n_own_tiles = pp->n_qtiles;
+  pp->n_own_tiles = (int)ceil_div(lq, HN_TILE);
   int max_spans = 4 + s->num_actions;
   if (sp) {
     if (sp->tile_q != HN_TILE || sp->tile_k != HN_TILE)
@@ -295,9 +295,10 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
     return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
+  const int want_tile = plan->sparse ? HN_TILE : hn::attn_dense_rows();
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
-      plan->head_tokens != c->head_tokens || plan->tile_q != HN_TILE ||
-      plan->n_qtiles != (int)ceil_div(lq, HN_TILE))
+      plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
+      plan->n_qtiles != (int)ceil_div(lq, want_tile))
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
@@ -314,6 +315,7 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.H = c->num_heads;
   p.lq = lq;
   p.n_qtiles = plan->n_qtiles;
+  p.tile_rows = plan->tile_q;
   p.max_spans = plan->max_spans;
   p.n_tasks = p.H * p.n_qtiles;
   p.tasks_per_xcd = (p.n_tasks + 7) / 8;

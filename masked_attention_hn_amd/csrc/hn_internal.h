@@ -71,6 +71,7 @@ struct AttnParams {
   int32_t H;
   int32_t lq;
   int32_t n_qtiles;
+  int32_t tile_rows;     // query rows per plan tile (selects the kernel instance)
   int32_t max_spans;
   int32_t n_tasks;
   int32_t tasks_per_xcd;
@@ -78,6 +79,7 @@ struct AttnParams {
   int32_t ring_cap;      // ring stride (tokens) per head = W*P
   float scale_log2;      // sm_scale * log2(e)
   int32_t txt_len;       // h + sum(a) text rows of the current segment
+  int32_t pad0;
   const int32_t* counts;
   const Span* spans;
   const __bf16* q;
@@ -132,6 +134,9 @@ struct DenseParams {
   int64_t frames_seen;
   uint8_t* out;
 };
+
+// Query rows per tile of a dense (keep-list free) plan; keep-list plans use HN_TILE.
+int attn_dense_rows();
 
 // Launchers (defined next to their kernels); return the HIP error of the launch.
 hipError_t launch_quant_append(const AppendParams& p, hipStream_t s);
