@@ -33,7 +33,9 @@
 //            probabilities stay <= 2^8 and the rescale is rare after the
 //            first tiles.  The result is exact algebra (same max in O and l).
 //   masks  = only partial tiles pay for masking: ragged tile ends and action
-//            tails whose row range does not cover all of a wave's rows.
+//            tails whose row range does not cover all of a wave's rows.  Full
+//            bf16 tiles take a lean path; INT8 and partial tiles share one
+//            general path (bf16 tiles carry unit scales in LDS for it).
 //   order  = the plan's span order, KT keys at a time, double-buffered: global
 //            loads of tile n+1 are in flight while tile n is computed.
 //   grid   = XCD-aware: block b runs on XCD b % 8, and each XCD gets a
@@ -233,6 +235,8 @@ __device__ inline void store_tile(Smem<C>& sm, int b, bool i8, const Prefetch<C>
   const int tid = threadIdx.x;
   uint32_t rows[C::VPT][4][4];  // V rows as 4 x (8 bf16) packed words
   if (!i8) {
+    // unit scales, so bf16 tiles can take the general (scaled) path too
+    if (tid < 2 * C::KT) (tid < C::KT ? sm.ks[b][tid] : sm.vs[b][tid - C::KT]) = 1.0f;
 #pragma unroll
     for (int c = 0; c < C::KCH; ++c) {
       const int key = c * (C::T / 16) + (tid >> 4), dch = tid & 15;
@@ -505,13 +509,10 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
       for (int q = 0; q < QB; ++q) row_ok[q] = row[q] >= cur.r0 && row[q] < cur.r1;
       const bool mask = (cur.nk < C::KT) || !rows_all;
       const float sl = p.scale_log2;
-      if (cur.src < SRC_TXT) {
-        if (mask) tile_math<C, true, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
-        else tile_math<C, true, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
-      } else {
-        if (mask) tile_math<C, false, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
-        else tile_math<C, false, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
-      }
+      // two code paths only (more would raise register pressure past two
+      // waves per SIMD): unmasked bf16 tiles, and everything else
+      if (cur.src < SRC_TXT || mask) tile_math<C, true, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
+      else tile_math<C, false, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
     }
 
     if (have_next) store_tile<C>(sm, buf ^ 1, nxt.src < SRC_TXT, pf);
