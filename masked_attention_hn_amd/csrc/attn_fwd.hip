@@ -307,8 +307,11 @@ struct RowState {
 };
 
 // One KT-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-//   I8   : the tile comes from the INT8 cache (per-key scales in LDS)
+//   I8   : general path: per-key scales from LDS (1 for bf16 tiles), masking
 //   MASK : some keys (ragged end) or rows (tail window) of the tile are invisible
+// The QK MFMAs of all 32-key blocks are issued first; then each block's
+// softmax runs while the next block's MFMAs are still in flight, and its PV
+// MFMAs run while the following block's softmax is computed.
 template <class C, bool I8, bool MASK>
 __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16x8 (&qreg)[C::QB][8],
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
@@ -333,24 +336,21 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
     }
   }
 
-  bf16x8 pb[QB][C::NT];
 #pragma unroll
-  for (int q = 0; q < QB; ++q) {
-    // scores in log2 units; element 4r+i of block kb is key kb*32 + 8r + 4g + i
-    float mx;
-    if (I8 || MASK) {
-      mx = -INFINITY;
-      const int nkg = row_ok[q] ? nk - 4 * g : INT_MIN;  // key visible iff kb*32+8r+i < nkg
+  for (int kb = 0; kb < KB; ++kb) {
+    bf16x8 pb[QB][2];
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
+    for (int q = 0; q < QB; ++q) {
+      // scores in log2 units; element 4r+i is key kb*32 + 8r + 4g + i
+      float mx;
+      if (I8 || MASK) {
+        mx = -INFINITY;
+        const int nkg = row_ok[q] ? nk - 4 * g : INT_MIN;  // key visible iff kb*32+8r+i < nkg
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float cc[4] = {scale_log2, scale_log2, scale_log2, scale_log2};
-          if (I8) {
-            const float4 ksc = *reinterpret_cast<const float4*>(&sm.ks[buf][kb * 32 + 8 * r + 4 * g]);
-            cc[0] = ksc.x * scale_log2; cc[1] = ksc.y * scale_log2;
-            cc[2] = ksc.z * scale_log2; cc[3] = ksc.w * scale_log2;
-          }
+          const float4 ksc = *reinterpret_cast<const float4*>(&sm.ks[buf][kb * 32 + 8 * r + 4 * g]);
+          const float cc[4] = {ksc.x * scale_log2, ksc.y * scale_log2, ksc.z * scale_log2,
+                               ksc.w * scale_log2};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             float v = s[q][kb][4 * r + i] * cc[i];
@@ -359,65 +359,74 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
             mx = fmaxf(mx, v);
           }
         }
+      } else {
+        // every key visible and one scale: take the max of the raw scores
+        float m0 = s[q][kb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s[q][kb][i]);
+        mx = m0 * scale_log2;
       }
-    } else {
-      // every key visible and one scale: take the max of the raw scores
-      float m0 = s[q][0][0];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m0 = fmaxf(m0, s[q][kb][i]);
-      mx = m0 * scale_log2;
-    }
-    mx = pair_max(mx);
+      mx = pair_max(mx);
 
-    // lazy rescale: move the running max only when it lags by more than the slack
-    if (__any(mx > st[q].m + RESCALE_SLACK)) {
-      const float m_new = fmaxf(st[q].m, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st[q].m - m_new);
-      st[q].m = m_new;
-      st[q].l *= alpha;
+      // lazy rescale: move the running max only when it lags by more than the slack
+      if (__any(mx > st[q].m + RESCALE_SLACK)) {
+        const float m_new = fmaxf(st[q].m, mx);
+        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st[q].m - m_new);
+        st[q].m = m_new;
+        st[q].l *= alpha;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[q][c] *= alpha;
-    }
-    const float m_use = (st[q].m == -INFINITY) ? 0.0f : st[q].m;
+        for (int c = 0; c < 4; ++c) acc[q][c] *= alpha;
+      }
+      const float m_use = (st[q].m == -INFINITY) ? 0.0f : st[q].m;
 
-    float psum = 0.0f;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
       float pv[16];
+      if (I8 || MASK) {
+        float psum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float vv[4] = {1.0f, 1.0f, 1.0f, 1.0f};
-        if (I8) {
+        for (int r = 0; r < 4; ++r) {
           const float4 vsc = *reinterpret_cast<const float4*>(&sm.vs[buf][kb * 32 + 8 * r + 4 * g]);
-          vv[0] = vsc.x; vv[1] = vsc.y; vv[2] = vsc.z; vv[3] = vsc.w;
-        }
+          const float vv[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float e2;
-          if (I8 || MASK) e2 = __builtin_amdgcn_exp2f(s[q][kb][4 * r + i] - m_use);
-          else e2 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][4 * r + i], scale_log2, -m_use));
-          psum += e2;
-          pv[4 * r + i] = I8 ? e2 * vv[i] : e2;
+          for (int i = 0; i < 4; ++i) {
+            const float e2 = __builtin_amdgcn_exp2f(s[q][kb][4 * r + i] - m_use);
+            psum += e2;
+            pv[4 * r + i] = e2 * vv[i];
+          }
         }
+        st[q].l += psum;
+        pb[q][0] = pack_p(pv);
+        pb[q][1] = pack_p(pv + 8);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][i], scale_log2, -m_use));
+        pb[q][0] = pack_p(pv);
+        pb[q][1] = pack_p(pv + 8);
+        // row sum of the bf16 probabilities the PV MFMA uses (dot with ones)
+        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        float l = st[q].l;
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const bf16x2 pp = {pb[q][h2][2 * j], pb[q][h2][2 * j + 1]};
+            l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
+          }
+        st[q].l = l;
       }
-      pb[q][2 * kb] = pack_p(pv);
-      pb[q][2 * kb + 1] = pack_p(pv + 8);
     }
-    st[q].l += psum;
-  }
 
-  // O^T += V^T P^T
+    // O^T += V^T P^T for this 32-key block
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int d = 32 * c + l32;
+    for (int c = 0; c < 4; ++c) {
+      const int d = 32 * c + l32;
 #pragma unroll
-    for (int t = 0; t < C::NT; ++t) {
-      const bf16x8 vv = ld8(vl + d * C::VP + 16 * t + 8 * g);
+      for (int t = 0; t < 2; ++t) {
+        const bf16x8 vv = ld8(vl + d * C::VP + 32 * kb + 16 * t + 8 * g);
 #pragma unroll
-      for (int q = 0; q < QB; ++q)
-        acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[q][t], acc[q][c], 0, 0, 0);
+        for (int q = 0; q < QB; ++q)
+          acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[q][t], acc[q][c], 0, 0, 0);
+      }
     }
   }
 }
@@ -548,17 +557,19 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   }
 }
 
-// Dense plans: 256-row blocks of 8 waves x 32 rows (two waves per SIMD, the
-// staging of each tile shared by 256 queries).  Keep-list plans: 128-row
-// blocks (the keep list's query tile), 4 waves, two blocks per CU.
+// Dense and keep-list plans both use 128-row blocks of 4 waves x 32 rows with
+// two blocks per CU (two waves per SIMD from independent blocks, which drift
+// out of phase so one block's MFMAs overlap the other's softmax).  Measured
+// alternatives: 8-wave 256-row blocks (c3/c4 slower), 4 waves x 64 rows at
+// one wave per SIMD (much slower), 128-key tiles (spill).
 #ifndef HN_DENSE_NW
-#define HN_DENSE_NW 8
+#define HN_DENSE_NW 4
 #endif
 #ifndef HN_DENSE_QB
 #define HN_DENSE_QB 1
 #endif
 #ifndef HN_DENSE_MINB
-#define HN_DENSE_MINB 1
+#define HN_DENSE_MINB 2
 #endif
 using DenseCfg = Cfg<HN_DENSE_NW, HN_DENSE_QB, 64>;
 using SparseCfg = Cfg<4, 1, 64>;

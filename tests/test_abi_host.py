@@ -111,7 +111,7 @@ def test_workspace_sizes_and_plan_checks():
 def test_attention_rejects_stale_plan():
     c = fake_cache()
     s = seg_c()
-    plan = hn.hn_tile_plan(FAKE, 256, 1, 6, 0, 0, 0, 0, -1)   # dense plans use 256-row tiles
+    plan = hn.hn_tile_plan(FAKE, 128, 1, 6, 0, 0, 0, 0, -1)   # 128-row query tiles
     fwd = hn._lib.hn_seg_attn_fwd
     args = [FAKE] * 6  # q, k_txt, v_txt, k_vid, v_vid, o
     plan.frames_seen = 24          # built for another cache state
