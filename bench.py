@@ -16,6 +16,7 @@ against 8 TB/s, with rotating buffers so the bytes come from HBM.
 cpu_baseline times the fp64 CPU oracle on a sample of the same workload.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -34,16 +35,44 @@ APPEND_BYTES_PER_ROW = 2 * 128 * 2 + 2 * 128 + 2 * 4   # 776
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps; the clock ramps over the first ~50 ms of work")
     ap.add_argument("--workload", default="c2", help="c2 (default), c3, c4 or c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=11700, help="query rows the oracle computes")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
-    ap.add_argument("--traffic", default=None,
-                    help="JSON {fetch_kib, write_kib, scale} per attention launch from counters")
     return ap.parse_args()
+
+
+KERNEL_SOURCES = ("masked_attention_hn_amd/csrc/attn_fwd.hip", "masked_attention_hn_amd/csrc/hn_internal.h")
+COUNTERS = os.path.join(ROOT, "profiles", "seg_attn_fwd_c2_counters.json")
+
+
+def kernel_sources_sha256():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def counter_traffic(workload):
+    """HBM bytes per attention launch from the stored FETCH_SIZE/WRITE_SIZE
+    counters, each scaled by what the counter reads for a plain 1 GiB device
+    copy; None when the counters were taken on other kernel sources or
+    another workload."""
+    if not os.path.exists(COUNTERS):
+        return None
+    with open(COUNTERS) as fh:
+        c = json.load(fh)
+    if c["workload"] != workload or c["kernel_sources_sha256"] != kernel_sources_sha256():
+        return None
+    gib_kib = float(1 << 20)
+    fetch = c["fetch_kib"] * gib_kib / c["copy_1gib_fetch_kib"]
+    write = c["write_kib"] * gib_kib / c["copy_1gib_write_kib"]
+    return round((fetch + write) * 1024)
 
 
 def visible_pairs(w, csr=None):
@@ -201,10 +230,7 @@ def main():
     app_med = app_ms[len(app_ms) // 2]
     append_gbs = append_bytes / (app_med * 1e-3) / 1e9
 
-    traffic = None
-    if args.traffic:
-        t = json.loads(args.traffic)
-        traffic = (t["fetch_kib"] + t["write_kib"]) * 1024 * t.get("scale", 1.0)
+    traffic = counter_traffic(args.workload)
 
     out = {
         "metric": METRIC,
@@ -273,6 +299,13 @@ def main():
             sample_pairs = pairs * len(rows) / w.current.video_len
         cpu_tflops = 4.0 * 128 * sample_pairs * w.heads / tc / 1e12
         ncores = len(os.sched_getaffinity(0))
+        try:
+            import threadpoolctl
+            blas = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+            if blas:
+                ncores = min(ncores, max(blas))
+        except ImportError:
+            pass
         out["cpu_baseline"] = {
             "value": round(cpu_tflops, 6),
             "unit": "TFLOP/s",

@@ -9,14 +9,14 @@
 //   block  = one (head, query tile of 32*QB*NW rows); NW waves, each owning
 //            QB blocks of 32 query rows.  Every K/V operand a wave reads from
 //            LDS feeds QB MFMAs, so QB = 2 halves the LDS traffic per flop.
-//   tile   = KT keys of one span of the tile plan, staged in LDS as bf16:
-//            K as [key][d] (row pitch 136 elements) and V transposed as
-//            [d][key] (row pitch KT+8 elements).  The transposed writes are
-//            conflict-free because the 16 lanes that write together hold 16
-//            different 4-key groups of the same 8 d values.
-//            Global loads are raw buffer loads: per-thread offsets are fixed
-//            for the block, each tile adds a scalar offset, and the buffer
-//            bound returns 0 past a source's end (no clamping, no branches).
+//   tile   = KT keys of one span of the tile plan, staged in LDS as bf16 in
+//            operand-major order, so that every MFMA operand a wave reads is
+//            64 consecutive slots (conflict-free); the V^T operand of the PV
+//            MFMA comes from gfx950's transposing ds_read_b64_tr_b16, so V is
+//            never transposed in registers.  bf16 tiles travel L2 -> LDS by
+//            buffer loads that write LDS directly (no registers, no ds_write);
+//            per-lane offsets are fixed for the block, each tile adds a scalar
+//            offset, and the buffer bound returns 0 past a source's end.
 //            INT8 tiles are read from HBM as int8 (half the bytes), converted
 //            to bf16 in registers on their way into LDS (int8 -> bf16 is exact),
 //            and their fp32 scales are applied after the MFMA: the key scale to
@@ -54,44 +54,44 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag
-constexpr int KP = D + 8;              // LDS pitch of a K row (bf16 elements)
-
 template <int NW_, int QB_, int KT_>
 struct Cfg {
   static constexpr int NW = NW_, QB = QB_, KT = KT_;
   static constexpr int T = 64 * NW;            // threads per block
   static constexpr int ROWS = 32 * QB * NW;    // query rows per block
   static constexpr int KB = KT / 32;           // 32-key blocks per tile
-  static constexpr int NT = KT / 16;           // PV MFMAs per d-block
-  static constexpr int VP = KT + 8;            // LDS pitch of a V^T row
-  static constexpr int NKQ = KT / 4;           // 4-key groups per tile
-  static constexpr int VU = NKQ * 16;          // V transpose units (4 keys x 8 d)
-  static constexpr int KCH = 16 * KT / T;      // bf16 K 16-byte chunks per thread
-  static constexpr int KCH8 = 8 * KT / T;      // INT8 K 16-byte chunks per thread
-  static constexpr int VPT = VU >= T ? VU / T : 1;  // V units per thread
-  static_assert(KT % 32 == 0 && KCH >= 1 && KCH8 >= 1, "tile shape");
-  static_assert(VU % T == 0 || T % VU == 0, "V units");
-  static_assert(T % NKQ == 0 || VU >= T, "V mapping");
+  static constexpr int KBLK = KB * 8;          // 1 KB K-operand blocks per tile
+  static constexpr int VBLK = 4 * KB * 2;      // 1 KB V-operand block pairs per tile
+  static constexpr int CH8 = 8 * KT / T;       // INT8 16-byte chunks per thread (K and V each)
+  static_assert(KT == 64, "tile shape");
+  static_assert(KBLK % NW == 0 && VBLK % NW == 0 && CH8 >= 1, "load split");
   static_assert(2 * KT <= T, "one scale per thread");
 };
 
+// LDS tiles are stored operand-major, so that every operand read of a wave is
+// 64 consecutive 16-byte (K) or 8-byte (V) slots.
+//   K block (kb, t), 1 KB: slot lane = 32g + q holds K[kb*32 + q][16t + 8g .. +8],
+//     the A operand of the QK MFMA of 16-d chunk t for lane (q, g).
+//   V blocks, 512 bytes each, indexed ((c*KB + kb)*2 + h)*2 + half: slot L
+//     (16-lane group G = L/16, s = L%16, g = L/32) holds the four values
+//     V[kb*32 + 16h + 8*half + 4g + s/4][32c + 16(G&1) + 4(s&3) .. +4]; one
+//     ds_read_b64_tr_b16 of the block gives lane (d, g) keys 16h + 8*half + 4g
+//     + {0..3} of column d, the keys its P register holds.
+// One LDS stage.  The kernel keeps two stages as separate __shared__ objects
+// (never one array indexed by a runtime stage number) so that the compiler can
+// tell the stage being read from the stage being filled by direct-to-LDS loads
+// and does not wait for those loads before reading.
 template <class C>
-struct Smem {
-  __bf16 k[2][C::KT * KP];
-  __bf16 vt[2][D * C::VP];
-  float ks[2][C::KT];
-  float vs[2][C::KT];
+struct Stage {
+  __bf16 k[C::KT * D];
+  __bf16 v[C::KT * D];
+  float ks[C::KT];
+  float vs[C::KT];
 };
 
 struct TileDesc {
   int src, kb, nk, r0, r1;
 };
-
-// Position of key `key` in a V^T row: bits 2 and 3 swapped, so the 8 keys one
-// lane group feeds to a PV MFMA are contiguous.
-__device__ inline int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 // max / sum of a value and its lane^32 partner
 __device__ inline float pair_max(float x) {
@@ -103,6 +103,8 @@ __device__ inline float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0.
 __device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
@@ -111,9 +113,9 @@ __device__ inline uint4 ld_b128(rsrc_t r, uint32_t voff, uint32_t soff) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
-__device__ inline uint2 ld_b64(rsrc_t r, uint32_t voff, uint32_t soff) {
-  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-  return make_uint2(v[0], v[1]);
+// 16 bytes per lane straight into LDS: lane l's bytes land at dst + 16 l.
+__device__ inline void ld_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
 // Two signed bytes of w (bytes b, b+1) -> packed bf16 pair (exact for |q| <= 127).
@@ -121,36 +123,36 @@ __device__ inline uint32_t i8x2_bf16(uint32_t w, int b) {
   const bf16x2 v = {(__bf16)(float)(int8_t)(w >> (8 * b)), (__bf16)(float)(int8_t)(w >> (8 * b + 8))};
   return __builtin_bit_cast(uint32_t, v);
 }
+// 16 INT8 codes -> 16 bf16 (two 16-byte words).
+__device__ inline void i8x16_bf16(uint4 w, uint4& lo, uint4& hi) {
+  lo.x = i8x2_bf16(w.x, 0); lo.y = i8x2_bf16(w.x, 2);
+  lo.z = i8x2_bf16(w.y, 0); lo.w = i8x2_bf16(w.y, 2);
+  hi.x = i8x2_bf16(w.z, 0); hi.y = i8x2_bf16(w.z, 2);
+  hi.z = i8x2_bf16(w.w, 0); hi.w = i8x2_bf16(w.w, 2);
+}
 
 template <class C>
-struct Prefetch {
-  uint4 k[C::KCH];
-  uint4 v[C::VPT][4];
+struct Prefetch {  // INT8 tiles only
+  uint4 k[C::CH8];
+  uint4 v[C::CH8];
   float sc;
 };
 
-// Buffer resources of one head's key/value sources and the per-thread
-// offsets of its share of a tile (both fixed for the whole block).
+// Buffer resources of one head's key/value sources and the per-lane offsets
+// of the operand-major loads (all fixed for the whole block).
 struct Sources {
   rsrc_t k_txt, v_txt, k_vid, v_vid;             // bf16, token-major
   rsrc_t k_heads, v_heads, ks_heads, vs_heads;   // INT8 head store + scales
   rsrc_t k_ring, v_ring, ks_ring, vs_ring;       // INT8 ring + scales
   uint32_t tok_bytes;                            // bf16 token stride = H * D * 2
-  uint32_t vo_kb, vo_vb;                         // bf16 K / V thread offsets
-  uint32_t vo_ki, vo_vi;                         // INT8 K / V thread offsets
-  uint32_t vo_sc;                                // scale thread offset
+  uint32_t vo_k, vo_v;                           // bf16 direct-load lane offsets
+  uint32_t vo_i;                                 // INT8 lane offset (row lane%64, 16 codes)
+  uint32_t vo_sc;                                // scale lane offset
 };
-
-// V transpose unit of thread tid (first of its VPT units): 4-key group kq and
-// 8-d chunk dc; further units of the thread add T / NKQ to dc.
-template <class C>
-__device__ inline int v_kq(int tid) { return tid % C::NKQ; }
-template <class C>
-__device__ inline int v_dc(int tid) { return tid / C::NKQ; }
 
 template <class C>
 __device__ inline void init_sources(const AttnParams& p, int h, Sources& S) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const uint32_t tb = (uint32_t)p.H * D * 2;
   S.tok_bytes = tb;
   const uint32_t hoff = (uint32_t)h * D * 2;
@@ -167,132 +169,122 @@ __device__ inline void init_sources(const AttnParams& p, int h, Sources& S) {
   S.v_ring = make_rsrc(p.ring_v + (int64_t)h * p.ring_cap * D, (uint32_t)p.ring_cap * D);
   S.ks_ring = make_rsrc(p.ring_ks + (int64_t)h * p.ring_cap, (uint32_t)p.ring_cap * 4);
   S.vs_ring = make_rsrc(p.ring_vs + (int64_t)h * p.ring_cap, (uint32_t)p.ring_cap * 4);
-  const int kq = v_kq<C>(tid), dc = v_dc<C>(tid);
-  S.vo_kb = (uint32_t)(tid >> 4) * tb + (tid & 15) * 16;   // key c*T/16 + tid/16, chunk tid%16
-  S.vo_vb = (uint32_t)(4 * kq) * tb + dc * 16;             // key 4kq + r, d chunk dc
-  S.vo_ki = (uint32_t)(tid >> 3) * D + (tid & 7) * 16;     // key c*T/8 + tid/8, 16 codes
-  S.vo_vi = (uint32_t)(4 * kq) * D + dc * 8;               // key 4kq + r, 8 codes
+  // K block slot lane = 32g + q  <-  row q, 16-byte chunk g (of the block's 32 bytes)
+  S.vo_k = (uint32_t)(lane & 31) * tb + (lane >> 5) * 16;
+  // V block pair: lane i feeds slots 2(i%32), 2(i%32)+1 of block half i/32:
+  //   row 8(i/32) + 4((i/16)%2) + (i/2)%4, column 16((i/8)%2) + 8(i%2)
+  S.vo_v = (uint32_t)(8 * (lane >> 5) + 4 * ((lane >> 4) & 1) + ((lane >> 1) & 3)) * tb +
+           (16 * ((lane >> 3) & 1) + 8 * (lane & 1)) * 2;
+  S.vo_i = (uint32_t)lane * D;
   S.vo_sc = (uint32_t)(tid % C::KT) * 4;
 }
 
+// bf16 tile: every K and V byte goes straight from L2 into its LDS slot.
 template <class C>
-__device__ inline bool v_active(int tid) { return C::VU >= C::T || tid < C::VU; }
-
-template <class C>
-__device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb, Prefetch<C>& pf) {
+__device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb, Stage<C>& sb) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const uint32_t base = (uint32_t)kb * S.tok_bytes;
 #pragma unroll
-  for (int c = 0; c < C::KCH; ++c) pf.k[c] = ld_b128(rk, S.vo_kb, base + c * (C::T / 16) * S.tok_bytes);
-  if (v_active<C>(threadIdx.x)) {
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        pf.v[i][r] = ld_b128(rv, S.vo_vb, base + r * S.tok_bytes + i * (C::T / C::NKQ) * 16);
+  for (int j = 0; j < C::KBLK / C::NW; ++j) {
+    const int blk = wave * (C::KBLK / C::NW) + j;          // (kb32, t) = (blk / 8, blk % 8)
+    ld_lds16(rk, &sb.k[blk * 512], S.vo_k, base + (blk >> 3) * 32 * S.tok_bytes + (blk & 7) * 32);
   }
-  pf.sc = 1.0f;
+#pragma unroll
+  for (int j = 0; j < C::VBLK / C::NW; ++j) {
+    const int pr = wave * (C::VBLK / C::NW) + j;           // ((c*KB + kb32)*2 + h)
+    const int c = pr / (2 * C::KB), kb32 = (pr / 2) % C::KB, h = pr & 1;
+    ld_lds16(rv, &sb.v[pr * 512], S.vo_v, base + (kb32 * 32 + 16 * h) * S.tok_bytes + 64 * c);
+  }
 }
 
 template <class C>
 __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rks, rsrc_t rvs, int kb,
                                int nk, Prefetch<C>& pf) {
-  const int tid = threadIdx.x;
+  static_assert(C::KT == 64, "one wave per scale vector");
+  // wave index made scalar so that offsets and descriptors stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t base = (uint32_t)kb * D;
 #pragma unroll
-  for (int c = 0; c < C::KCH8; ++c) pf.k[c] = ld_b128(rk, S.vo_ki, base + c * (C::T / 8) * D);
-  if (v_active<C>(tid)) {
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint2 w = ld_b64(rv, S.vo_vi, base + r * D + i * (C::T / C::NKQ) * 8);
-        pf.v[i][r] = make_uint4(w.x, w.y, 0, 0);
-      }
+  for (int c = 0; c < C::CH8; ++c) {
+    const uint32_t dch = c * (C::T / 64) + wave;  // 16-code chunk of row lane%64
+    pf.k[c] = ld_b128(rk, S.vo_i, base + dch * 16);
+    pf.v[c] = ld_b128(rv, S.vo_i, base + dch * 16);
   }
   float sc = 0.0f;
-  if (tid < 2 * C::KT) {
+  if (wave < 2) {  // wave 0: key scales, wave 1: value scales
     const float v = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(tid < C::KT ? rks : rvs, S.vo_sc, (uint32_t)kb * 4, 0));
-    sc = (tid % C::KT) < nk ? v : 0.0f;
+        __builtin_amdgcn_raw_buffer_load_b32(wave == 0 ? rks : rvs, S.vo_sc, (uint32_t)kb * 4, 0));
+    sc = (threadIdx.x % C::KT) < nk ? v : 0.0f;
   }
   pf.sc = sc;
 }
 
-// Global -> registers for one tile.  Keys past the span end read other finite
-// data (or 0 past the buffer end) and are masked by the math; their value
-// scales are zeroed so that a 0 probability times the scale stays 0.
+// INT8 tile: convert and write the operand-major layouts (row r = tid % 64,
+// codes [16 dch, 16 dch + 16)).
 template <class C>
-__device__ inline void load_tile(const Sources& S, const TileDesc& t, Prefetch<C>& pf) {
-  if (t.src == SRC_VID) load_bf16<C>(S, S.k_vid, S.v_vid, t.kb, pf);
-  else if (t.src == SRC_TXT) load_bf16<C>(S, S.k_txt, S.v_txt, t.kb, pf);
-  else if (t.src == SRC_RING) load_i8<C>(S, S.k_ring, S.v_ring, S.ks_ring, S.vs_ring, t.kb, t.nk, pf);
-  else load_i8<C>(S, S.k_heads, S.v_heads, S.ks_heads, S.vs_heads, t.kb, t.nk, pf);
+__device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
+  const int tid = threadIdx.x;
+  const int r = tid & 63;
+  const int kb32 = r >> 5, q32 = r & 31;
+  // V slot coordinates of row r
+  const int h = (r >> 4) & 1, half = (r >> 3) & 1, g = (r >> 2) & 1, qq = r & 3;
+#pragma unroll
+  for (int c8 = 0; c8 < C::CH8; ++c8) {
+    const int dch = (c8 * C::T + tid) >> 6;
+    uint4 lo, hi;
+    i8x16_bf16(pf.k[c8], lo, hi);
+    // d chunks 2dch (g=0) and 2dch+1 (g=1) of K block (kb32, t = dch)
+    __bf16* kblk = &sb.k[(kb32 * 8 + dch) * 512];
+    *reinterpret_cast<uint4*>(kblk + q32 * 8) = lo;
+    *reinterpret_cast<uint4*>(kblk + (32 + q32) * 8) = hi;
+    i8x16_bf16(pf.v[c8], lo, hi);
+    // columns 16 dch .. +16 -> c = dch / 2, G&1 = dch % 2, slots 16G + 4qq + {0..3}
+    const int c = dch >> 1, G = 2 * g + (dch & 1);
+    __bf16* vblk = &sb.v[(((c * C::KB + kb32) * 2 + h) * 2 + half) * 256];
+    *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4) = lo;
+    *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4 + 8) = hi;
+  }
+  if (tid < C::KT) sb.ks[tid] = pf.sc;
+  else if (tid < 2 * C::KT) sb.vs[tid - C::KT] = pf.sc;
 }
 
-// Registers -> LDS buffer `b` (bf16 K rows, bf16 V^T rows, scales).
+// Start loading tile t into LDS buffer b: bf16 tiles land in LDS directly
+// (their unit scales are written here); INT8 tiles go to registers and are
+// stored by finish_tile.
 template <class C>
-__device__ inline void store_tile(Smem<C>& sm, int b, bool i8, const Prefetch<C>& pf) {
+__device__ inline void start_tile(const Sources& S, const TileDesc& t, Stage<C>& sb, Prefetch<C>& pf) {
   const int tid = threadIdx.x;
-  uint32_t rows[C::VPT][4][4];  // V rows as 4 x (8 bf16) packed words
-  if (!i8) {
-    // unit scales, so bf16 tiles can take the general (scaled) path too
-    if (tid < 2 * C::KT) (tid < C::KT ? sm.ks[b][tid] : sm.vs[b][tid - C::KT]) = 1.0f;
-#pragma unroll
-    for (int c = 0; c < C::KCH; ++c) {
-      const int key = c * (C::T / 16) + (tid >> 4), dch = tid & 15;
-      *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 8]) = pf.k[c];
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rows[i][r][0] = pf.v[i][r].x; rows[i][r][1] = pf.v[i][r].y;
-        rows[i][r][2] = pf.v[i][r].z; rows[i][r][3] = pf.v[i][r].w;
-      }
+  if (t.src >= SRC_TXT) {
+    // unit scales first: a store after the direct loads into the same stage
+    // would make the compiler wait for those loads
+    if (tid < 2 * C::KT) (tid < C::KT ? sb.ks[tid] : sb.vs[tid - C::KT]) = 1.0f;
+    if (t.src == SRC_VID) load_bf16<C>(S, S.k_vid, S.v_vid, t.kb, sb);
+    else load_bf16<C>(S, S.k_txt, S.v_txt, t.kb, sb);
+  } else if (t.src == SRC_RING) {
+    load_i8<C>(S, S.k_ring, S.v_ring, S.ks_ring, S.vs_ring, t.kb, t.nk, pf);
   } else {
-#pragma unroll
-    for (int c = 0; c < C::KCH8; ++c) {
-      const int key = c * (C::T / 8) + (tid >> 3), dch = tid & 7;
-      const uint4 w = pf.k[c];
-      uint4 lo, hi;
-      lo.x = i8x2_bf16(w.x, 0); lo.y = i8x2_bf16(w.x, 2);
-      lo.z = i8x2_bf16(w.y, 0); lo.w = i8x2_bf16(w.y, 2);
-      hi.x = i8x2_bf16(w.z, 0); hi.y = i8x2_bf16(w.z, 2);
-      hi.z = i8x2_bf16(w.w, 0); hi.w = i8x2_bf16(w.w, 2);
-      *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 16]) = lo;
-      *reinterpret_cast<uint4*>(&sm.k[b][key * KP + dch * 16 + 8]) = hi;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VPT; ++i)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        rows[i][r][0] = i8x2_bf16(pf.v[i][r].x, 0); rows[i][r][1] = i8x2_bf16(pf.v[i][r].x, 2);
-        rows[i][r][2] = i8x2_bf16(pf.v[i][r].y, 0); rows[i][r][3] = i8x2_bf16(pf.v[i][r].y, 2);
-      }
-    if (tid < C::KT) sm.ks[b][tid] = pf.sc;
-    else if (tid < 2 * C::KT) sm.vs[b][tid - C::KT] = pf.sc;
+    load_i8<C>(S, S.k_heads, S.v_heads, S.ks_heads, S.vs_heads, t.kb, t.nk, pf);
   }
-  if (!v_active<C>(tid)) return;
-  // transpose 4 keys x 8 d into 8 rows of V^T, 4 keys (8 bytes) each
-  const int pos = vt_pos(4 * v_kq<C>(tid));
-#pragma unroll
-  for (int i = 0; i < C::VPT; ++i) {
-    const int dc = v_dc<C>(tid) + i * (C::T / C::NKQ);
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const int d0 = dc * 8 + 2 * w;
-      uint2 e, o;
-      e.x = __builtin_amdgcn_perm(rows[i][1][w], rows[i][0][w], 0x05040100u);
-      e.y = __builtin_amdgcn_perm(rows[i][3][w], rows[i][2][w], 0x05040100u);
-      o.x = __builtin_amdgcn_perm(rows[i][1][w], rows[i][0][w], 0x07060302u);
-      o.y = __builtin_amdgcn_perm(rows[i][3][w], rows[i][2][w], 0x07060302u);
-      *reinterpret_cast<uint2*>(&sm.vt[b][d0 * C::VP + pos]) = e;
-      *reinterpret_cast<uint2*>(&sm.vt[b][(d0 + 1) * C::VP + pos]) = o;
-    }
-  }
+}
+template <class C>
+__device__ inline void finish_tile(const TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf) {
+  if (t.src < SRC_TXT) store_i8<C>(sb, pf);
 }
 
 __device__ inline bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+// Two ds_read_b64_tr_b16 (elements 0..3 from p0, 4..7 from p1).  Within each
+// 16-lane group, output lane i element k is element (i & 3) of the 8 bytes that
+// lane 4k + (i >> 2) addresses.
+__device__ inline bf16x8 tr_read8(const __bf16* p0, const __bf16* p1) {
+  const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p0));
+  const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p1));
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+  const s16x8 r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, r);
+}
 
 __device__ inline bf16x8 pack_p(const float* x) {
   bf16x8 r;
@@ -313,14 +305,14 @@ struct RowState {
 // softmax runs while the next block's MFMAs are still in flight, and its PV
 // MFMAs run while the following block's softmax is computed.
 template <class C, bool I8, bool MASK>
-__device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16x8 (&qreg)[C::QB][8],
+__device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8],
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
                                           float scale_log2, int nk, const bool (&row_ok)[C::QB]) {
   constexpr int QB = C::QB, KB = C::KB;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5, l32 = lane & 31;
-  const __bf16* kl = sm.k[buf];
-  const __bf16* vl = sm.vt[buf];
+  const __bf16* kl = sb.k + lane * 8;   // slot of this lane in every K block
+  const __bf16* vl = sb.v + lane * 4;   // slot of this lane in every V block
 
   f32x16 s[QB][KB];
 #pragma unroll
@@ -329,7 +321,7 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
     for (int q = 0; q < QB; ++q) s[q][kb] = f32x16{};
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
-      const bf16x8 kk = ld8(kl + (kb * 32 + l32) * KP + 16 * t + 8 * g);
+      const bf16x8 kk = ld8(kl + (kb * 8 + t) * 512);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
         s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk, qreg[q][t], s[q][kb], 0, 0, 0);
@@ -348,7 +340,7 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
         const int nkg = row_ok[q] ? nk - 4 * g : INT_MIN;  // key visible iff kb*32+8r+i < nkg
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float4 ksc = *reinterpret_cast<const float4*>(&sm.ks[buf][kb * 32 + 8 * r + 4 * g]);
+          const float4 ksc = *reinterpret_cast<const float4*>(&sb.ks[kb * 32 + 8 * r + 4 * g]);
           const float cc[4] = {ksc.x * scale_log2, ksc.y * scale_log2, ksc.z * scale_log2,
                                ksc.w * scale_log2};
 #pragma unroll
@@ -384,7 +376,7 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float4 vsc = *reinterpret_cast<const float4*>(&sm.vs[buf][kb * 32 + 8 * r + 4 * g]);
+          const float4 vsc = *reinterpret_cast<const float4*>(&sb.vs[kb * 32 + 8 * r + 4 * g]);
           const float vv[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -416,13 +408,16 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
       }
     }
 
-    // O^T += V^T P^T for this 32-key block
+    // O^T += V^T P^T for this 32-key block.  The A operand (V^T) comes from
+    // two transposing reads of V blocks (c, kb, t, half = 0/1): lane (d, g)
+    // receives keys kb*32 + 16t + 4g + {0..3} and + 8 + {0..3} of column d,
+    // the keys its P register holds.
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int d = 32 * c + l32;
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const bf16x8 vv = ld8(vl + d * C::VP + 32 * kb + 16 * t + 8 * g);
+        const __bf16* a = vl + ((c * KB + kb) * 2 + t) * 512;
+        const bf16x8 vv = tr_read8(a, a + 256);
 #pragma unroll
         for (int q = 0; q < QB; ++q)
           acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv, pb[q][t], acc[q][c], 0, 0, 0);
@@ -434,7 +429,8 @@ __device__ __forceinline__ void tile_math(const Smem<C>& sm, int buf, const bf16
 template <class C, int MIN_BLOCKS>
 __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnParams p) {
   constexpr int QB = C::QB;
-  __shared__ Smem<C> sm;
+  __shared__ Stage<C> stage0;
+  __shared__ Stage<C> stage1;
   const int task = (blockIdx.x & 7) * p.tasks_per_xcd + (blockIdx.x >> 3);
   if (task >= p.n_tasks) return;  // whole block leaves before any barrier
   const int h = task / p.n_qtiles;
@@ -479,7 +475,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   // tile iterator over the spans (block-uniform)
   int e = 0;
   int kpos = n_spans > 0 ? spans[0].k0 : 0;
-  auto next_tile = [&](TileDesc& t) -> bool {
+  auto next_tile = [&](TileDesc& t) __attribute__((always_inline)) -> bool {
     if (e >= n_spans) return false;
     const Span s = spans[e];
     t.src = s.src;
@@ -495,19 +491,19 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     return true;
   };
 
+  // One pipeline step: compute tile `cur` from stage `sc` while tile `nxt`
+  // streams into stage `sn`; the stages alternate, unrolled by two so that
+  // each step's stages are distinct objects.
   TileDesc cur, nxt;
   bool have = next_tile(cur);
-  Prefetch<C> pf;
   if (have) {
-    load_tile<C>(S, cur, pf);
-    store_tile<C>(sm, 0, cur.src < SRC_TXT, pf);
+    Prefetch<C> pf;
+    start_tile<C>(S, cur, stage0, pf);
+    finish_tile<C>(cur, stage0, pf);
   }
+  __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of this thread have landed
   __syncthreads();
-  int buf = 0;
-  while (have) {
-    const bool have_next = next_tile(nxt);
-    if (have_next) load_tile<C>(S, nxt, pf);
-
+  auto compute = [&](const Stage<C>& sc) __attribute__((always_inline)) {
     // rows of this wave that see the tile; skip the math if none does
     const int wrows = 32 * QB;
     const bool wave_live = (cur.r0 < wrow0 + wrows) && (cur.r1 > wrow0);
@@ -520,15 +516,28 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
       const float sl = p.scale_log2;
       // two code paths only (more would raise register pressure past two
       // waves per SIMD): unmasked bf16 tiles, and everything else
-      if (cur.src < SRC_TXT || mask) tile_math<C, true, true>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
-      else tile_math<C, false, false>(sm, buf, qreg, acc, st, sl, cur.nk, row_ok);
+      if (cur.src < SRC_TXT || mask) tile_math<C, true, true>(sc, qreg, acc, st, sl, cur.nk, row_ok);
+      else tile_math<C, false, false>(sc, qreg, acc, st, sl, cur.nk, row_ok);
     }
-
-    if (have_next) store_tile<C>(sm, buf ^ 1, nxt.src < SRC_TXT, pf);
+  };
+  // The prefetch registers of an INT8 tile are fresh in every step (not
+  // carried around the loop), so no copies of them sit between the loads and
+  // the math of the current tile.
+  auto step = [&](const Stage<C>& sc, Stage<C>& sn) __attribute__((always_inline)) {
+    const bool have_next = next_tile(nxt);
+    Prefetch<C> pf;
+    if (have_next) start_tile<C>(S, nxt, sn, pf);
+    compute(sc);
+    if (have_next) finish_tile<C>(nxt, sn, pf);
+    __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of this thread have landed
     __syncthreads();
     cur = nxt;
     have = have_next;
-    buf ^= 1;
+  };
+  while (have) {
+    step(stage0, stage1);
+    if (!have) break;
+    step(stage1, stage0);
   }
 
   // epilogue: O = acc / l, lse = (m + log2 l) * ln 2
