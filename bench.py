@@ -50,11 +50,21 @@ KERNEL_SOURCES = ("masked_attention_hn_amd/csrc/attn_fwd.hip", "masked_attention
 COUNTERS = os.path.join(ROOT, "profiles", "seg_attn_fwd_c2_counters.json")
 
 
+def normalize_source(src):
+    """C++ source text with comments removed and whitespace collapsed."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_sources_sha256():
+    """SHA-256 of the attention kernel's normalized sources, so that only a
+    change of code invalidates stored counters."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            h.update(normalize_source(fh.read()).encode())
     return h.hexdigest()
 
 

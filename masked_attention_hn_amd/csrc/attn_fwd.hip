@@ -8,7 +8,9 @@
 // Work decomposition (template <NW, QB, KT>)
 //   block  = one (head, query tile of 32*QB*NW rows); NW waves, each owning
 //            QB blocks of 32 query rows.  Every K/V operand a wave reads from
-//            LDS feeds QB MFMAs, so QB = 2 halves the LDS traffic per flop.
+//            LDS feeds QB MFMAs; QB = 2 would halve the LDS traffic per flop
+//            but needs more than 256 VGPRs (one wave per SIMD), which measured
+//            slower, so the instances below use QB = 1 and two blocks per CU.
 //   tile   = KT keys of one span of the tile plan, staged in LDS as bf16 in
 //            operand-major order, so that every MFMA operand a wave reads is
 //            64 consecutive slots (conflict-free); the V^T operand of the PV
