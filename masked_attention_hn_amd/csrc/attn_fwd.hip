@@ -19,10 +19,10 @@
 //            buffer loads that write LDS directly (no registers, no ds_write);
 //            per-lane offsets are fixed for the block, each tile adds a scalar
 //            offset, and the buffer bound returns 0 past a source's end.
-//            INT8 tiles are read from HBM as int8 (half the bytes), converted
-//            to bf16 in registers on their way into LDS (int8 -> bf16 is exact),
-//            and their fp32 scales are applied after the MFMA: the key scale to
-//            the score column, the value scale to the probability.
+//            INT8 tiles are read from HBM as int8 (half the bytes) with their
+//            per-token fp32 scales and dequantized to bf16 (code x scale,
+//            correctly rounded in fp32, then rounded to bf16) in registers on
+//            their way into LDS, so the math never sees a scale.
 //   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then holds
 //            the tile's keys for one query, so the row max/sum are in-lane plus
 //            one v_permlane32_swap with lane^32); online softmax in the log2
@@ -36,8 +36,7 @@
 //            first tiles.  The result is exact algebra (same max in O and l).
 //   masks  = only partial tiles pay for masking: ragged tile ends and action
 //            tails whose row range does not cover all of a wave's rows.  Full
-//            bf16 tiles take a lean path; INT8 and partial tiles share one
-//            general path (bf16 tiles carry unit scales in LDS for it).
+//            tiles of any source take a lean path.
 //   order  = the plan's span order, KT keys at a time, double-buffered: global
 //            loads of tile n+1 are in flight while tile n is computed.
 //   grid   = XCD-aware: block b runs on XCD b % 8, and each XCD gets a
@@ -87,8 +86,6 @@ template <class C>
 struct Stage {
   __bf16 k[C::KT * D];
   __bf16 v[C::KT * D];
-  float ks[C::KT];
-  float vs[C::KT];
 };
 
 struct TileDesc {
@@ -120,24 +117,35 @@ __device__ inline void ld_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t sof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
-// Two signed bytes of w (bytes b, b+1) -> packed bf16 pair (exact for |q| <= 127).
-__device__ inline uint32_t i8x2_bf16(uint32_t w, int b) {
-  const bf16x2 v = {(__bf16)(float)(int8_t)(w >> (8 * b)), (__bf16)(float)(int8_t)(w >> (8 * b + 8))};
-  return __builtin_bit_cast(uint32_t, v);
+// Four INT8 codes of w times the row scale sc -> two packed bf16 pairs.
+// With u = q + 128 (the codes' bytes xor 0x80), fma(u, sc, -128 sc) is the
+// correctly rounded fp32 product q * sc (128 sc is exact), then rounded to bf16.
+__device__ inline void i8x4_dequant(uint32_t w, float sc, float m128, uint32_t& p0, uint32_t& p1) {
+  const uint32_t u = w ^ 0x80808080u;
+  const float f0 = __builtin_fmaf((float)(u & 0xffu), sc, m128);
+  const float f1 = __builtin_fmaf((float)((u >> 8) & 0xffu), sc, m128);
+  const float f2 = __builtin_fmaf((float)((u >> 16) & 0xffu), sc, m128);
+  const float f3 = __builtin_fmaf((float)(u >> 24), sc, m128);
+  const bf16x2 a = {(__bf16)f0, (__bf16)f1};
+  const bf16x2 b = {(__bf16)f2, (__bf16)f3};
+  p0 = __builtin_bit_cast(uint32_t, a);
+  p1 = __builtin_bit_cast(uint32_t, b);
 }
-// 16 INT8 codes -> 16 bf16 (two 16-byte words).
-__device__ inline void i8x16_bf16(uint4 w, uint4& lo, uint4& hi) {
-  lo.x = i8x2_bf16(w.x, 0); lo.y = i8x2_bf16(w.x, 2);
-  lo.z = i8x2_bf16(w.y, 0); lo.w = i8x2_bf16(w.y, 2);
-  hi.x = i8x2_bf16(w.z, 0); hi.y = i8x2_bf16(w.z, 2);
-  hi.z = i8x2_bf16(w.w, 0); hi.w = i8x2_bf16(w.w, 2);
+// 16 INT8 codes of one row -> 16 dequantized bf16 (two 16-byte words).
+__device__ inline void i8x16_dequant(uint4 w, float sc, uint4& lo, uint4& hi) {
+  const float m128 = -128.0f * sc;
+  i8x4_dequant(w.x, sc, m128, lo.x, lo.y);
+  i8x4_dequant(w.y, sc, m128, lo.z, lo.w);
+  i8x4_dequant(w.z, sc, m128, hi.x, hi.y);
+  i8x4_dequant(w.w, sc, m128, hi.z, hi.w);
 }
 
 template <class C>
 struct Prefetch {  // INT8 tiles only
   uint4 k[C::CH8];
   uint4 v[C::CH8];
-  float sc;
+  float ks, vs;  // scales of this thread's row
+  bool ok;       // the row is one of the tile's valid keys
 };
 
 // Buffer resources of one head's key/value sources and the per-lane offsets
@@ -202,7 +210,7 @@ __device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb,
 template <class C>
 __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rks, rsrc_t rvs, int kb,
                                int nk, Prefetch<C>& pf) {
-  static_assert(C::KT == 64, "one wave per scale vector");
+  static_assert(C::KT == 64, "row = lane");
   // wave index made scalar so that offsets and descriptors stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t base = (uint32_t)kb * D;
@@ -212,13 +220,13 @@ __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rk
     pf.k[c] = ld_b128(rk, S.vo_i, base + dch * 16);
     pf.v[c] = ld_b128(rv, S.vo_i, base + dch * 16);
   }
-  float sc = 0.0f;
-  if (wave < 2) {  // wave 0: key scales, wave 1: value scales
-    const float v = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(wave == 0 ? rks : rvs, S.vo_sc, (uint32_t)kb * 4, 0));
-    sc = (threadIdx.x % C::KT) < nk ? v : 0.0f;
-  }
-  pf.sc = sc;
+  // every thread dequantizes row lane%64, so every thread needs its scales
+  const bool ok = (int)(threadIdx.x & 63) < nk;
+  const float ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, S.vo_sc, (uint32_t)kb * 4, 0));
+  const float vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, S.vo_sc, (uint32_t)kb * 4, 0));
+  pf.ks = ks;  // used only after the current tile's math: no wait here
+  pf.vs = vs;
+  pf.ok = ok;
 }
 
 // INT8 tile: convert and write the operand-major layouts (row r = tid % 64,
@@ -230,24 +238,24 @@ __device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
   const int kb32 = r >> 5, q32 = r & 31;
   // V slot coordinates of row r
   const int h = (r >> 4) & 1, half = (r >> 3) & 1, g = (r >> 2) & 1, qq = r & 3;
+  // rows past the tile's valid keys become zeros
+  const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
 #pragma unroll
   for (int c8 = 0; c8 < C::CH8; ++c8) {
     const int dch = (c8 * C::T + tid) >> 6;
     uint4 lo, hi;
-    i8x16_bf16(pf.k[c8], lo, hi);
+    i8x16_dequant(pf.k[c8], ks, lo, hi);
     // d chunks 2dch (g=0) and 2dch+1 (g=1) of K block (kb32, t = dch)
     __bf16* kblk = &sb.k[(kb32 * 8 + dch) * 512];
     *reinterpret_cast<uint4*>(kblk + q32 * 8) = lo;
     *reinterpret_cast<uint4*>(kblk + (32 + q32) * 8) = hi;
-    i8x16_bf16(pf.v[c8], lo, hi);
+    i8x16_dequant(pf.v[c8], vs, lo, hi);
     // columns 16 dch .. +16 -> c = dch / 2, G&1 = dch % 2, slots 16G + 4qq + {0..3}
     const int c = dch >> 1, G = 2 * g + (dch & 1);
     __bf16* vblk = &sb.v[(((c * C::KB + kb32) * 2 + h) * 2 + half) * 256];
     *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4) = lo;
     *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4 + 8) = hi;
   }
-  if (tid < C::KT) sb.ks[tid] = pf.sc;
-  else if (tid < 2 * C::KT) sb.vs[tid - C::KT] = pf.sc;
 }
 
 // Start loading tile t into LDS buffer b: bf16 tiles land in LDS directly
@@ -257,9 +265,6 @@ template <class C>
 __device__ inline void start_tile(const Sources& S, const TileDesc& t, Stage<C>& sb, Prefetch<C>& pf) {
   const int tid = threadIdx.x;
   if (t.src >= SRC_TXT) {
-    // unit scales first: a store after the direct loads into the same stage
-    // would make the compiler wait for those loads
-    if (tid < 2 * C::KT) (tid < C::KT ? sb.ks[tid] : sb.vs[tid - C::KT]) = 1.0f;
     if (t.src == SRC_VID) load_bf16<C>(S, S.k_vid, S.v_vid, t.kb, sb);
     else load_bf16<C>(S, S.k_txt, S.v_txt, t.kb, sb);
   } else if (t.src == SRC_RING) {
@@ -301,12 +306,12 @@ struct RowState {
 };
 
 // One KT-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
-//   I8   : general path: per-key scales from LDS (1 for bf16 tiles), masking
 //   MASK : some keys (ragged end) or rows (tail window) of the tile are invisible
-// The QK MFMAs of all 32-key blocks are issued first; then each block's
-// softmax runs while the next block's MFMAs are still in flight, and its PV
-// MFMAs run while the following block's softmax is computed.
-template <class C, bool I8, bool MASK>
+// The QK MFMAs of the whole tile are issued first, then one rescale decision
+// is taken from the maxima of all its 32-key blocks, so that the exponentials
+// and PV MFMAs of the blocks form one straight-line region the compiler can
+// interleave.  The row sum adds the bf16 probabilities the PV MFMA consumes.
+template <class C, bool MASK>
 __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8],
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
                                           float scale_log2, int nk, const bool (&row_ok)[C::QB]) {
@@ -330,90 +335,71 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
     }
   }
 
+  // one rescale decision per tile: maxima of every block first
+  float m_use[QB];
+#pragma unroll
+  for (int q = 0; q < QB; ++q) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      if (MASK) {
+        const int nkg = row_ok[q] ? nk - 4 * g : INT_MIN;  // key visible iff kb*32+8r+i < nkg
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            float v = s[q][kb][4 * r + i] * scale_log2;
+            if (kb * 32 + 8 * r + i >= nkg) v = -INFINITY;
+            s[q][kb][4 * r + i] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+        float m0 = s[q][kb][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s[q][kb][i]);
+        mx = fmaxf(mx, m0 * scale_log2);
+      }
+    }
+    mx = pair_max(mx);
+    if (__any(mx > st[q].m + RESCALE_SLACK)) {
+      const float m_new = fmaxf(st[q].m, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st[q].m - m_new);
+      st[q].m = m_new;
+      st[q].l *= alpha;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[q][c] *= alpha;
+    }
+    m_use[q] = (st[q].m == -INFINITY) ? 0.0f : st[q].m;
+  }
+
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     bf16x8 pb[QB][2];
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
-      // scores in log2 units; element 4r+i is key kb*32 + 8r + 4g + i
-      float mx;
-      if (I8 || MASK) {
-        mx = -INFINITY;
-        const int nkg = row_ok[q] ? nk - 4 * g : INT_MIN;  // key visible iff kb*32+8r+i < nkg
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 ksc = *reinterpret_cast<const float4*>(&sb.ks[kb * 32 + 8 * r + 4 * g]);
-          const float cc[4] = {ksc.x * scale_log2, ksc.y * scale_log2, ksc.z * scale_log2,
-                               ksc.w * scale_log2};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = s[q][kb][4 * r + i] * cc[i];
-            if (MASK && kb * 32 + 8 * r + i >= nkg) v = -INFINITY;
-            s[q][kb][4 * r + i] = v;
-            mx = fmaxf(mx, v);
-          }
-        }
-      } else {
-        // every key visible and one scale: take the max of the raw scores
-        float m0 = s[q][kb][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s[q][kb][i]);
-        mx = m0 * scale_log2;
-      }
-      mx = pair_max(mx);
-
-      // lazy rescale: move the running max only when it lags by more than the slack
-      if (__any(mx > st[q].m + RESCALE_SLACK)) {
-        const float m_new = fmaxf(st[q].m, mx);
-        const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st[q].m - m_new);
-        st[q].m = m_new;
-        st[q].l *= alpha;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[q][c] *= alpha;
-      }
-      const float m_use = (st[q].m == -INFINITY) ? 0.0f : st[q].m;
-
+      // masked path: scores are already scaled (and -inf where invisible)
       float pv[16];
-      if (I8 || MASK) {
-        float psum = 0.0f;
+      if (MASK) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float4 vsc = *reinterpret_cast<const float4*>(&sb.vs[kb * 32 + 8 * r + 4 * g]);
-          const float vv[4] = {vsc.x, vsc.y, vsc.z, vsc.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float e2 = __builtin_amdgcn_exp2f(s[q][kb][4 * r + i] - m_use);
-            psum += e2;
-            pv[4 * r + i] = e2 * vv[i];
-          }
-        }
-        st[q].l += psum;
-        pb[q][0] = pack_p(pv);
-        pb[q][1] = pack_p(pv + 8);
+        for (int i = 0; i < 16; ++i) pv[i] = __builtin_amdgcn_exp2f(s[q][kb][i] - m_use[q]);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][i], scale_log2, -m_use));
-        pb[q][0] = pack_p(pv);
-        pb[q][1] = pack_p(pv + 8);
-        // row sum of the bf16 probabilities the PV MFMA uses (dot with ones)
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-        float l = st[q].l;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const bf16x2 pp = {pb[q][h2][2 * j], pb[q][h2][2 * j + 1]};
-            l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
-          }
-        st[q].l = l;
+          pv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][i], scale_log2, -m_use[q]));
       }
+      pb[q][0] = pack_p(pv);
+      pb[q][1] = pack_p(pv + 8);
+      const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+      float l = st[q].l;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pp = {pb[q][h2][2 * j], pb[q][h2][2 * j + 1]};
+          l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
+        }
+      st[q].l = l;
     }
-
-    // O^T += V^T P^T for this 32-key block.  The A operand (V^T) comes from
-    // two transposing reads of V blocks (c, kb, t, half = 0/1): lane (d, g)
-    // receives keys kb*32 + 16t + 4g + {0..3} and + 8 + {0..3} of column d,
-    // the keys its P register holds.
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -516,10 +502,10 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
       for (int q = 0; q < QB; ++q) row_ok[q] = row[q] >= cur.r0 && row[q] < cur.r1;
       const bool mask = (cur.nk < C::KT) || !rows_all;
       const float sl = p.scale_log2;
-      // two code paths only (more would raise register pressure past two
-      // waves per SIMD): unmasked bf16 tiles, and everything else
-      if (cur.src < SRC_TXT || mask) tile_math<C, true, true>(sc, qreg, acc, st, sl, cur.nk, row_ok);
-      else tile_math<C, false, false>(sc, qreg, acc, st, sl, cur.nk, row_ok);
+      // INT8 tiles sit in LDS already dequantized, so every source shares
+      // the two paths: full tiles and masked ones
+      if (mask) tile_math<C, true>(sc, qreg, acc, st, sl, cur.nk, row_ok);
+      else tile_math<C, false>(sc, qreg, acc, st, sl, cur.nk, row_ok);
     }
   };
   // The prefetch registers of an INT8 tile are fresh in every step (not
