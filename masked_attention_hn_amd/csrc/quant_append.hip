@@ -8,10 +8,12 @@
 //   q     = round_half_even(x / scale) (correctly rounded fp32 quotient),
 //           clamped to [-127, 127]; a zero row stores scale 0 and q 0.
 //
-// The kernel is HBM-bound streaming: 16 lanes own one row (8 bf16 = 16 bytes
-// of K and 16 of V per lane), the row max is a 16-lane butterfly, and each lane
-// writes 8 int8 codes per tensor.  Consecutive 16-lane groups take the heads
-// of one token, so each wave reads 4 x 256 contiguous bytes per tensor.
+// The kernel is HBM-bound streaming: 8 lanes own one row (16 bf16 = 32 bytes
+// of K and 32 of V per lane), the row max is an 8-lane butterfly, and each
+// lane writes 16 int8 codes (one 16-byte store) per tensor.  Consecutive
+// 8-lane groups take the heads of one token, so each wave reads 8 x 256
+// contiguous bytes per tensor.  (16-byte stores measured 9-13% faster than
+// 8-byte ones; non-temporal loads/stores and two rows per lane group slower.)
 // The division is the compiler's correctly rounded fp32 divide (no fast-math);
 // fp32 denormals are preserved so subnormal scales quantize exactly.
 #include "hn_internal.h"
@@ -37,14 +39,6 @@ __device__ inline uint2 quant8(const float (&x)[8], float scale, bool zero) {
   return r;
 }
 
-__device__ inline float row_amax16(float m) {
-  m = fmaxf(m, __shfl_xor(m, 1));
-  m = fmaxf(m, __shfl_xor(m, 2));
-  m = fmaxf(m, __shfl_xor(m, 4));
-  m = fmaxf(m, __shfl_xor(m, 8));
-  return m;
-}
-
 __device__ inline void unpack8(uint4 w, float (&x)[8], float& amax) {
   x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x);
   x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
@@ -56,11 +50,18 @@ __device__ inline void unpack8(uint4 w, float (&x)[8], float& amax) {
   amax = m;
 }
 
+__device__ inline float row_amax8(float m) {
+  m = fmaxf(m, __shfl_xor(m, 1));
+  m = fmaxf(m, __shfl_xor(m, 2));
+  m = fmaxf(m, __shfl_xor(m, 4));
+  return m;
+}
+
 __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
-  const int lane16 = threadIdx.x & 15;
-  const int64_t unit = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int lane8 = threadIdx.x & 7;
+  const int64_t unit = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
   const int64_t rows = (int64_t)p.head_len + p.n_vid;
-  // Whole 16-lane groups leave together, so the butterflies below stay inside
+  // Whole 8-lane groups leave together, so the butterflies below stay inside
   // active lanes.
   if (unit >= rows * p.H) return;
   const int t = (int)(unit / p.H);
@@ -85,23 +86,27 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
     ks = p.k_vid; vs = p.v_vid;
     kd = p.ring_k; vd = p.ring_v; kds = p.ring_ks; vds = p.ring_vs;
   }
-  const int64_t src = (src_row * p.H + h) * D + lane16 * 8;
-  const uint4 kw = *reinterpret_cast<const uint4*>(ks + src);
-  const uint4 vw = *reinterpret_cast<const uint4*>(vs + src);
+  const int64_t src = (src_row * p.H + h) * D + lane8 * 16;
+  const uint4 kw0 = *reinterpret_cast<const uint4*>(ks + src);
+  const uint4 kw1 = *reinterpret_cast<const uint4*>(ks + src + 8);
+  const uint4 vw0 = *reinterpret_cast<const uint4*>(vs + src);
+  const uint4 vw1 = *reinterpret_cast<const uint4*>(vs + src + 8);
 
-  float kx[8], vx[8], ka, va;
-  unpack8(kw, kx, ka);
-  unpack8(vw, vx, va);
-  ka = row_amax16(ka);
-  va = row_amax16(va);
+  float kx0[8], kx1[8], vx0[8], vx1[8], ka0, ka1, va0, va1;
+  unpack8(kw0, kx0, ka0);
+  unpack8(kw1, kx1, ka1);
+  unpack8(vw0, vx0, va0);
+  unpack8(vw1, vx1, va1);
+  const float ka = row_amax8(fmaxf(ka0, ka1));
+  const float va = row_amax8(fmaxf(va0, va1));
   const float ksc = ka / 127.0f;
   const float vsc = va / 127.0f;
-  const uint2 kq = quant8(kx, ksc, ka == 0.0f);
-  const uint2 vq = quant8(vx, vsc, va == 0.0f);
+  const uint2 kq0 = quant8(kx0, ksc, ka == 0.0f), kq1 = quant8(kx1, ksc, ka == 0.0f);
+  const uint2 vq0 = quant8(vx0, vsc, va == 0.0f), vq1 = quant8(vx1, vsc, va == 0.0f);
 
-  *reinterpret_cast<uint2*>(kd + dst_row * D + lane16 * 8) = kq;
-  *reinterpret_cast<uint2*>(vd + dst_row * D + lane16 * 8) = vq;
-  if (lane16 == 0) {
+  *reinterpret_cast<uint4*>(kd + dst_row * D + lane8 * 16) = make_uint4(kq0.x, kq0.y, kq1.x, kq1.y);
+  *reinterpret_cast<uint4*>(vd + dst_row * D + lane8 * 16) = make_uint4(vq0.x, vq0.y, vq1.x, vq1.y);
+  if (lane8 == 0) {
     kds[dst_row] = ka == 0.0f ? 0.0f : ksc;
     vds[dst_row] = va == 0.0f ? 0.0f : vsc;
   }
@@ -112,7 +117,7 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
 hipError_t launch_quant_append(const AppendParams& p, hipStream_t s) {
   const int64_t units = ((int64_t)p.head_len + p.n_vid) * p.H;
   if (units == 0) return hipSuccess;
-  const int64_t blocks = (units + 15) / 16;
+  const int64_t blocks = (units + 31) / 32;
   hipLaunchKernelGGL(quant_append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
