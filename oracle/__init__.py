@@ -37,8 +37,17 @@ Hy-Nomas world model):
   Readings where the pages are silent: tail windows are half-open
   [f0, f1) in local latent frames and overlap by OR; the window keeps video
   frames whose global index is >= (first frame of the query segment) - W;
-  heads of every earlier segment stay visible; queries are the video tokens
-  of the query segment.
+  heads of every earlier segment stay visible.
+
+* mask_text(): the same visibility for the query segment's text-stream
+  queries (its head and tail tokens; the MMDiT attends text and video
+  jointly).  The segment-causal rule holds for them as stated (own segment
+  and earlier ones only, earlier video inside the window); the pages give
+  tails' time windows only in terms of video frames, so the reading for
+  text queries is: a tail token sees its own tail and no other, a head token
+  sees no tail (an action description never reaches the head that later
+  segments keep).  Keep lists concern video query tiles only, so text
+  queries attend densely.
 
 * attention(): plain softmax attention in fp64 per head over the masked
   full sequence: s = (q . k) * sm_scale, masked scores are -inf,
@@ -191,6 +200,43 @@ def mask(w: Workload, rows: Optional[Sequence[int]] = None,
     return vis
 
 
+def mask_text(w: Workload, rows: Optional[Sequence[int]] = None,
+              tab: Optional[dict] = None) -> np.ndarray:
+    """Explicit boolean visibility [len(rows)][L] over the full sequence for
+    text-stream queries: rows index the query segment's text tokens (head,
+    then tails in order)."""
+    if tab is None:
+        tab = token_table(w)
+    S = w.query_segment
+    cur = w.current
+    rows = np.arange(cur.text_len) if rows is None else np.asarray(rows, dtype=np.int64)
+    g0 = _first_frame(w, S)
+
+    # tail index of each query row (-1 for head rows)
+    q_tail = np.full(cur.text_len, -1, dtype=np.int64)
+    r = cur.head_len
+    for j, a in enumerate(cur.action_len):
+        q_tail[r:r + a] = j
+        r += a
+    qj = q_tail[rows]
+
+    seg, kind, tail, gframe = tab["seg"], tab["kind"], tab["tail"], tab["gframe"]
+    earlier = seg < S
+    same = seg == S
+    if w.window is None:
+        in_window = np.ones_like(earlier)
+    else:
+        in_window = gframe >= g0 - w.window
+    col_vis = (earlier & (kind == HEAD)) | (earlier & (kind == VIDEO) & in_window) \
+        | (same & (kind == HEAD)) | (same & (kind == VIDEO))
+    vis = np.broadcast_to(col_vis, (len(rows), len(seg))).copy()
+    own_tail = same & (kind == TAIL)
+    idx = np.nonzero(own_tail)[0]
+    if len(idx):
+        vis[:, idx] = (qj[:, None] >= 0) & (qj[:, None] == tail[idx][None, :])
+    return vis
+
+
 # ------------------------------------------------------------------ values
 def key_values(w: Workload, data: dict):
     """Keys and values of the whole sequence as fp64 [L][H][D].
@@ -216,18 +262,21 @@ def key_values(w: Workload, data: dict):
 # --------------------------------------------------------------- attention
 def attention(w: Workload, data: dict, rows: Optional[Sequence[int]] = None,
               sm_scale: Optional[float] = None, chunk: int = 256,
-              kv: Optional[tuple] = None):
+              kv: Optional[tuple] = None, queries: str = "video"):
     """Masked softmax attention in fp64.
 
-    Returns (O [nrows][H][D], lse [H][nrows], rowsum [H][nrows]); lse is the
-    natural log of sum(exp(s)) over visible keys, rowsum the sum of the
-    normalized weights.
+    queries: "video" (rows of Q_vid, mask()) or "text" (rows of Q_txt,
+    mask_text()).  Returns (O [nrows][H][D], lse [H][nrows], rowsum
+    [H][nrows]); lse is the natural log of sum(exp(s)) over visible keys,
+    rowsum the sum of the normalized weights.
     """
     H, D = w.heads, w.head_dim
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(D)
+    if queries not in ("video", "text"):
+        raise ValueError(queries)
     K, V = kv if kv is not None else key_values(w, data)
-    Q = bf16_bits_to_f32(data["q_vid"]).astype(np.float64)
+    Q = bf16_bits_to_f32(data["q_vid" if queries == "video" else "q_txt"]).astype(np.float64)
     nq = Q.shape[0]
     rows = np.arange(nq) if rows is None else np.asarray(rows, dtype=np.int64)
     O = np.zeros((len(rows), H, D))
@@ -239,7 +288,7 @@ def attention(w: Workload, data: dict, rows: Optional[Sequence[int]] = None,
     tab = token_table(w)
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
-        vis = mask(w, r, csr, tab)
+        vis = mask(w, r, csr, tab) if queries == "video" else mask_text(w, r, tab)
         for h in range(H):
             s = (Q[r, h, :] @ Kh[h].T) * sm_scale
             s = np.where(vis, s, -np.inf)
@@ -251,6 +300,11 @@ def attention(w: Workload, data: dict, rows: Optional[Sequence[int]] = None,
             lse[h, c0:c0 + len(r)] = m[:, 0] + np.log(l[:, 0])
             rsum[h, c0:c0 + len(r)] = np.sum(p, axis=1)
     return O, lse, rsum
+
+
+def effective_flops_text(w: Workload) -> float:
+    """4 * D * (visible (text query, key) pairs) * H."""
+    return 4.0 * w.head_dim * int(mask_text(w).sum()) * w.heads
 
 
 def effective_flops(w: Workload, data: Optional[dict] = None) -> float:

@@ -73,6 +73,39 @@ def brute_visible(w, tok, q_frame, q_row, csr=None):
     return True
 
 
+def brute_visible_text(w, tok, q_tail):
+    """Visibility for a text-stream query of the query segment; q_tail is the
+    query's tail index, or None for a description-head token."""
+    S = w.query_segment
+    s, kind, tail, lf, gf, where, row, p = tok
+    g0 = sum(seg.frames for seg in w.segments[:S])
+    if s > S:
+        return False
+    if s < S:
+        if kind == "head":
+            return True
+        if kind == "tail":
+            return False
+        return w.window is None or gf >= g0 - w.window
+    if kind == "head":
+        return True
+    if kind == "tail":
+        return q_tail is not None and tail == q_tail
+    return True
+
+
+def text_query_tail(seg, r):
+    """Tail index of text row r of a segment (None for head rows)."""
+    if r < seg.head_len:
+        return None
+    r -= seg.head_len
+    for j, a in enumerate(seg.action_len):
+        if r < a:
+            return j
+        r -= a
+    raise IndexError(r)
+
+
 def _value_row(w, data, tok, h, which):
     S = w.query_segment
     s, kind, tail, lf, gf, where, row, p = tok
@@ -83,8 +116,9 @@ def _value_row(w, data, tok, h, which):
     return [float(bf16_to_fraction(int(b))) for b in bits]
 
 
-def brute_attention(w, data, rows=None, sm_scale=None):
-    """Returns (O[r][h][d], lse[h][r]) as nested Python lists."""
+def brute_attention(w, data, rows=None, sm_scale=None, queries="video"):
+    """Returns (O[r][h][d], lse[h][r]) as nested Python lists; queries is
+    "video" or "text" (the query segment's head and tail tokens)."""
     S = w.query_segment
     cur = w.segments[S]
     D = w.head_dim
@@ -92,7 +126,7 @@ def brute_attention(w, data, rows=None, sm_scale=None):
         sm_scale = 1.0 / math.sqrt(D)
     toks = _tokens(w)
     csr = data.get("csr") if w.sparse_keep is not None else None
-    nq = cur.frames * cur.tokens_per_frame
+    nq = cur.frames * cur.tokens_per_frame if queries == "video" else cur.text_len
     rows = list(range(nq)) if rows is None else list(rows)
     cache = {}
 
@@ -105,10 +139,15 @@ def brute_attention(w, data, rows=None, sm_scale=None):
     O = [[None] * w.heads for _ in rows]
     lse = [[None] * len(rows) for _ in range(w.heads)]
     for ri, r in enumerate(rows):
-        f = r // cur.tokens_per_frame
-        vis = [i for i, t in enumerate(toks) if brute_visible(w, t, f, r, csr)]
+        if queries == "video":
+            f = r // cur.tokens_per_frame
+            vis = [i for i, t in enumerate(toks) if brute_visible(w, t, f, r, csr)]
+        else:
+            qj = text_query_tail(cur, r)
+            vis = [i for i, t in enumerate(toks) if brute_visible_text(w, t, qj)]
+        qname = "q_vid" if queries == "video" else "q_txt"
         for h in range(w.heads):
-            q = [float(bf16_to_fraction(int(b))) for b in data["q_vid"][r, h, :]]
+            q = [float(bf16_to_fraction(int(b))) for b in data[qname][r, h, :]]
             scores = []
             for i in vis:
                 k = val(i, h, "k")

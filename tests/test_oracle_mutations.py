@@ -124,3 +124,43 @@ def test_attention_unquantized_history_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "dequantize", lambda q, s: q.astype(np.float64) * 0 + 1e-3)
     with pytest.raises(AssertionError):
         TA.test_brute_force_c1("c1")
+
+
+# ---- text-stream queries: plausible mistakes in mask_text are caught by its pins
+import test_oracle_text as TT  # noqa: E402
+
+_real_mask_text = oracle.mask_text
+
+
+def _text_mask_with(post):
+    def m(w, rows=None, tab=None):
+        vis = _real_mask_text(w, rows, tab)
+        tab = oracle.token_table(w) if tab is None else tab
+        return post(w, vis, tab)
+    return m
+
+
+def _text_all_own_tails(w, vis, tab):
+    vis[:, (tab["seg"] == w.query_segment) & (tab["kind"] == oracle.TAIL)] = True
+    return vis
+
+
+def _text_no_history_video(w, vis, tab):
+    vis[:, (tab["seg"] < w.query_segment) & (tab["kind"] == oracle.VIDEO)] = False
+    return vis
+
+
+def _text_no_own_tail(w, vis, tab):
+    vis[:, (tab["seg"] == w.query_segment) & (tab["kind"] == oracle.TAIL)] = False
+    return vis
+
+
+@pytest.mark.parametrize("post,pin,arg", [
+    (_text_all_own_tails, TT.test_text_visible_counts, ("c2", 12468, 12596)),
+    (_text_no_history_video, TT.test_text_visible_counts, ("c3", 45312, 45440)),
+    (_text_no_own_tail, TT.test_text_visible_counts, ("c1", 192, 200)),
+])
+def test_text_mask_mutations_are_caught(monkeypatch, post, pin, arg):
+    monkeypatch.setattr(oracle, "mask_text", _text_mask_with(post))
+    with pytest.raises(AssertionError):
+        pin(*arg)

@@ -189,8 +189,9 @@ def generate(w: Workload) -> Dict[str, object]:
     """Draw the inputs of a workload.
 
     Draw order: for every segment in sequence order, K_txt, V_txt, K_vid,
-    V_vid (each [tokens][H][D]); then Q_vid of the query segment.  Queries
-    are always N(0,1); keys and values follow w.kv_dist.
+    V_vid (each [tokens][H][D]); then Q_vid of the query segment, then its
+    Q_txt (text-stream queries: head and tail tokens).  Queries are always
+    N(0,1); keys and values follow w.kv_dist.
     """
     rng = np.random.default_rng(w.seed)
     H, D = w.heads, w.head_dim
@@ -203,7 +204,8 @@ def generate(w: Workload) -> Dict[str, object]:
             "v_vid": _draw(rng, (s.video_len, H, D), w.kv_dist),
         })
     q = _draw(rng, (w.current.video_len, H, D), "normal")
-    out = {"segments": segs, "q_vid": q}
+    qt = _draw(rng, (w.current.text_len, H, D), "normal")
+    out = {"segments": segs, "q_vid": q, "q_txt": qt}
     if w.sparse_keep is not None:
         out["csr"] = block_sparse_csr(w)
     return out
