@@ -85,6 +85,19 @@ def counter_traffic(workload):
     return round((fetch + write) * 1024)
 
 
+def visible_pairs_text(w):
+    """Unmasked (text query, key) pairs per head, from the layout (no oracle):
+    every text row sees earlier heads, kept history video, its own head and
+    video; a tail row also sees its own tail."""
+    S = w.query_segment
+    cur = w.current
+    g0 = sum(s.frames for s in w.segments[:S])
+    kept = g0 if w.window is None else min(g0, w.window)
+    base = sum(s.head_len for s in w.segments[:S]) + kept * cur.tokens_per_frame \
+        + cur.head_len + cur.video_len
+    return cur.text_len * base + sum(a * a for a in cur.action_len)
+
+
 def visible_pairs(w, csr=None):
     """Unmasked (query, key) pairs per head, from the layout (no oracle)."""
     S = w.query_segment
@@ -242,6 +255,37 @@ def main():
 
     traffic = counter_traffic(args.workload)
 
+    # the same call with the segment's text queries added (one launch for both)
+    joint = None
+    if w.current.text_len > 0:
+        cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
+        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c)
+        q_txt = to_dev(data["q_txt"])
+        o_txt = torch.empty_like(q_txt)
+        pairs_t = visible_pairs_text(w)
+        assert plan_c.visible_pairs_text == pairs_t, (plan_c.visible_pairs_text, pairs_t)
+        n_j = max(10, args.steps // 4)
+        ej0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_j)]
+        ej1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_j)]
+        for i in range(n_j):
+            ej0[i].record(stream)
+            hn.hn_seg_attn_fwd(cache, seg, plan, q, k_txt, v_txt, k_vid, v_vid, o,
+                               q_txt=q_txt, o_txt=o_txt)
+            ej1[i].record(stream)
+        torch.cuda.synchronize()
+        j_ms = sum(a.elapsed_time(b) for a, b in zip(ej0, ej1)) / n_j
+        j_flops = 4.0 * 128 * (pairs + pairs_t) * w.heads
+        joint = {
+            "what": "video + text-stream queries in one hn_seg_attn_fwd launch",
+            "text_queries": w.current.text_len,
+            "visible_pairs_text_per_head": pairs_t,
+            "effective_flop": j_flops,
+            "avg_launch_ms": round(j_ms, 4),
+            "achieved": round(j_flops / (j_ms * 1e-3) / 1e12, 3),
+            "unit": "TFLOP/s",
+            "frac": round(j_flops / (j_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        }
+
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -281,6 +325,7 @@ def main():
             "traffic": traffic,
             "avg_launch_ms": round(attn_avg, 4),
         },
+        "joint": joint,
         "append": {
             "kernel": "quant_append_kernel",
             "bound": "hbm",

@@ -185,24 +185,29 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
 /* Tile plan for one (cache state, segment, keep list); filled by
  * hn_attn_mask_build in TILE_PLAN mode and consumed by hn_seg_attn_fwd.
  * It may be reused by every attention call of the segment (all blocks and
- * denoising steps with the same keep list). */
+ * denoising steps with the same keep list).  Tiles 0 .. n_qtiles-1 cover
+ * the video queries, tiles n_qtiles .. n_qtiles+n_text_tiles-1 the text
+ * queries (head and tails). */
 typedef struct hn_tile_plan {
   const void* dev;            /* = the workspace the plan was written to */
   int32_t tile_q;             /* query rows per plan tile */
-  int32_t n_qtiles;
+  int32_t n_qtiles;           /* video query tiles: ceil(F*P / tile_q) */
+  int32_t n_text_tiles;       /* text query tiles: ceil((h + sum a) / tile_q) */
   int32_t max_spans;          /* span slots per query tile */
   int32_t seg_index;          /* cache/segment state the plan was built for */
-  int64_t frames_seen;
   int32_t head_tokens;
+  int64_t frames_seen;
   int32_t sparse;             /* 1 if a keep list was merged */
-  int64_t visible_pairs;      /* unmasked (query, key) pairs per head; -1 if sparse */
+  int32_t reserved0;
+  int64_t visible_pairs;      /* unmasked (video query, key) pairs per head; -1 if sparse */
+  int64_t visible_pairs_text; /* unmasked (text query, key) pairs per head */
 } hn_tile_plan;
 
 /* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments). */
 size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg,
                               const hn_block_sparse* sparse);
 
-/* Build the attention mask of the current segment's video queries.
+/* Build the attention mask of the current segment's queries.
  *
  * Visibility of key k for the video query at local frame f
  * ([T] "架构": segment-causal and action-aware attention; [H] warning under
@@ -215,6 +220,11 @@ size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg
  *   own video                         : always (bidirectional in a segment)
  *   later segments                    : never (not in the cache yet)
  *   with a keep list: video keys only in the query tile's kept tiles.
+ * Text queries (the segment's own head and tail tokens, which the MMDiT
+ * attends jointly with its video) follow the same segment-causal rule; tail
+ * windows are stated only for video frames, so the reading taken is: a token
+ * of tail j sees tail j and no other tail, a head token sees no tail.  Keep
+ * lists concern video query tiles only; text queries attend densely.
  *
  * TILE_PLAN: `out` is the workspace (>= hn_attn_workspace_size bytes, device,
  *   16-byte aligned).  For every query tile a kernel writes the list of key
@@ -222,7 +232,8 @@ size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg
  *   partial (a row range then restricts it); empty spans are dropped.  `plan`
  *   is filled.  row0/nrows are ignored.
  * DENSE: `out` is uint8 [nrows][Lk] (device) for query rows
- *   [row0, row0 + nrows), in the canonical key order
+ *   [row0, row0 + nrows) -- rows [0, F*P) are the video queries, rows
+ *   [F*P, F*P + h + sum(a)) the text queries -- in the canonical key order
  *   [history heads, oldest segment first | history video in the window,
  *    oldest frame first | own head | own tails | own video],
  *   Lk = head_tokens + kept_frames*P + h + sum(a) + F*P; 1 = visible.  It is
@@ -234,9 +245,10 @@ hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
                              int32_t row0, int32_t nrows, void* out, size_t out_bytes,
                              hn_tile_plan* plan, hipStream_t stream);
 
-/* Attention of the current segment's video queries over the cache and the
- * segment's own text and video, with one softmax over the union of visible
- * keys (the mask of hn_attn_mask_build):
+/* Attention of the current segment's video queries (and, if q_txt is given,
+ * its text queries) over the cache and the segment's own text and video,
+ * with one softmax over the union of visible keys (the mask of
+ * hn_attn_mask_build); one launch covers both query sets:
  *   O[q] = sum_k softmax_k(sm_scale * Q[q].K[k]) V[k]
  * History keys/values are the dequantized INT8 values q*scale; the segment's
  * own keys/values are used as given (quantization is storage-only,
@@ -246,17 +258,22 @@ hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
  * plan         : from hn_attn_mask_build(TILE_PLAN) for this exact cache
  *                state and segment, workspace still intact; else HN_ERR_ORDER
  * q_vid        : bf16 [F*P][H][D]
+ * q_txt        : bf16 [h + sum(a)][H][D] text queries, or NULL to skip them
  * k_txt, v_txt : bf16 [h + sum(a)][H][D] (may be NULL if h + sum(a) == 0)
  * k_vid, v_vid : bf16 [F*P][H][D]
  * o_vid        : bf16 [F*P][H][D] (output; must not alias the inputs)
- * lse          : fp32 [H][F*P] natural-log softmax normaliser, or NULL
+ * o_txt        : bf16 [h + sum(a)][H][D] output of the text queries; required
+ *                iff q_txt is given and h + sum(a) > 0
+ * lse, lse_txt : fp32 [H][F*P] / [H][h + sum(a)] natural-log softmax
+ *                normalisers, or NULL
  * sm_scale     : score scale, normally 1/sqrt(128)
  */
 hn_status hn_seg_attn_fwd(const hn_kv_cache* cache, const hn_seg_layout* seg,
-                          const hn_tile_plan* plan, const void* q_vid,
+                          const hn_tile_plan* plan, const void* q_vid, const void* q_txt,
                           const void* k_txt, const void* v_txt,
                           const void* k_vid, const void* v_vid,
-                          void* o_vid, float* lse, float sm_scale, hipStream_t stream);
+                          void* o_vid, void* o_txt, float* lse, float* lse_txt,
+                          float sm_scale, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -68,9 +68,11 @@ class hn_block_sparse(ctypes.Structure):
 
 class hn_tile_plan(ctypes.Structure):
     _fields_ = [("dev", _vp), ("tile_q", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
-                ("max_spans", ctypes.c_int32), ("seg_index", ctypes.c_int32),
-                ("frames_seen", ctypes.c_int64), ("head_tokens", ctypes.c_int32),
-                ("sparse", ctypes.c_int32), ("visible_pairs", ctypes.c_int64)]
+                ("n_text_tiles", ctypes.c_int32), ("max_spans", ctypes.c_int32),
+                ("seg_index", ctypes.c_int32), ("head_tokens", ctypes.c_int32),
+                ("frames_seen", ctypes.c_int64), ("sparse", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("visible_pairs", ctypes.c_int64),
+                ("visible_pairs_text", ctypes.c_int64)]
 
 
 _S = ctypes.c_int
@@ -94,8 +96,11 @@ _lib.hn_attn_mask_build.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(
                                     ctypes.POINTER(hn_tile_plan), _vp]
 _lib.hn_attn_mask_build.restype = _S
 _lib.hn_seg_attn_fwd.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
-                                 ctypes.POINTER(hn_tile_plan), _vp, _vp, _vp, _vp, _vp, _vp,
-                                 _vp, ctypes.c_float, _vp]
+                                 ctypes.POINTER(hn_tile_plan),
+                                 _vp, _vp,            # q_vid, q_txt
+                                 _vp, _vp, _vp, _vp,  # k_txt, v_txt, k_vid, v_vid
+                                 _vp, _vp, _vp, _vp,  # o_vid, o_txt, lse, lse_txt
+                                 ctypes.c_float, _vp]
 _lib.hn_seg_attn_fwd.restype = _S
 
 EXPORTS = ["hn_status_string", "hn_last_error", "hn_kv_cache_sizes", "hn_kv_cache_reset",
@@ -261,6 +266,10 @@ class Plan:
     def visible_pairs(self) -> int:
         return self.c.visible_pairs
 
+    @property
+    def visible_pairs_text(self) -> int:
+        return self.c.visible_pairs_text
+
 
 def build_plan(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None,
                workspace: Optional[torch.Tensor] = None, stream=None) -> Plan:
@@ -274,6 +283,8 @@ def build_plan(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = N
 
 def dense_mask(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None,
                row0: int = 0, nrows: Optional[int] = None, stream=None) -> torch.Tensor:
+    """Rows [0, video_len) are the video queries, [video_len, video_len + text_len)
+    the text queries."""
     nrows = seg.video_len - row0 if nrows is None else nrows
     kept = min(cache.frames_seen, cache.c.window_frames)
     lk = cache.head_tokens + kept * cache.c.tokens_per_frame + seg.text_len + seg.video_len
@@ -284,12 +295,14 @@ def dense_mask(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = N
 
 def hn_seg_attn_fwd(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, k_txt, v_txt, k_vid, v_vid,
                     o_vid: torch.Tensor, lse: Optional[torch.Tensor] = None,
-                    sm_scale: Optional[float] = None, stream=None):
+                    sm_scale: Optional[float] = None, stream=None, q_txt=None,
+                    o_txt: Optional[torch.Tensor] = None, lse_txt: Optional[torch.Tensor] = None):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(HEAD_DIM)
     _check(_lib.hn_seg_attn_fwd(ctypes.byref(cache.c), ctypes.byref(seg.c), ctypes.byref(plan.c),
-                                _ptr(q_vid), _ptr(k_txt), _ptr(v_txt), _ptr(k_vid), _ptr(v_vid),
-                                _ptr(o_vid), _ptr(lse), float(sm_scale), _stream(stream)))
+                                _ptr(q_vid), _ptr(q_txt), _ptr(k_txt), _ptr(v_txt), _ptr(k_vid),
+                                _ptr(v_vid), _ptr(o_vid), _ptr(o_txt), _ptr(lse), _ptr(lse_txt),
+                                float(sm_scale), _stream(stream)))
 
 
 def seg_attn(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, k_txt, v_txt, k_vid, v_vid,
@@ -301,3 +314,17 @@ def seg_attn(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, k_txt, v_txt, k_
         lse = torch.empty((cache.c.num_heads, seg.video_len), dtype=torch.float32, device="cuda")
     hn_seg_attn_fwd(cache, seg, plan, q_vid, k_txt, v_txt, k_vid, v_vid, o, lse, sm_scale, stream)
     return (o, lse) if with_lse else o
+
+
+def seg_attn_joint(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, q_txt, k_txt, v_txt, k_vid,
+                   v_vid, sm_scale: Optional[float] = None, stream=None):
+    """Video and text queries in one hn_seg_attn_fwd call; returns
+    (o_vid, o_txt, lse_vid, lse_txt)."""
+    H = cache.c.num_heads
+    o = torch.empty_like(q_vid)
+    o_txt = torch.empty_like(q_txt)
+    lse = torch.empty((H, seg.video_len), dtype=torch.float32, device="cuda")
+    lse_txt = torch.empty((H, seg.text_len), dtype=torch.float32, device="cuda")
+    hn_seg_attn_fwd(cache, seg, plan, q_vid, k_txt, v_txt, k_vid, v_vid, o, lse, sm_scale, stream,
+                    q_txt=q_txt, o_txt=o_txt, lse_txt=lse_txt)
+    return o, o_txt, lse, lse_txt

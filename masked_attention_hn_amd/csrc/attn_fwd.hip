@@ -421,8 +421,15 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   __shared__ Stage<C> stage1;
   const int task = (blockIdx.x & 7) * p.tasks_per_xcd + (blockIdx.x >> 3);
   if (task >= p.n_tasks) return;  // whole block leaves before any barrier
-  const int h = task / p.n_qtiles;
-  const int qt = task - h * p.n_qtiles;
+  const int h = task / p.n_tiles;
+  const int tile = task - h * p.n_tiles;
+  // plan tiles: video query tiles, then text query tiles (own head and tails)
+  const bool text = tile >= p.n_qtiles;
+  const int qt = text ? tile - p.n_qtiles : tile;  // tile within its query set
+  const int lq = text ? p.lq_txt : p.lq;
+  const __bf16* qsrc = text ? p.q_txt : p.q;
+  __bf16* odst = text ? p.o_txt : p.o;
+  float* lse_dst = text ? p.lse_txt : p.lse;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   bf16x8 qreg[QB][8];
   {
     const uint32_t tb = (uint32_t)p.H * D * 2;
-    const rsrc_t rq = make_rsrc(p.q + h * D, (uint32_t)p.lq * tb - (uint32_t)h * D * 2);
+    const rsrc_t rq = make_rsrc(qsrc + h * D, (uint32_t)lq * tb - (uint32_t)h * D * 2);
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
@@ -457,8 +464,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     st[q].l = 0.0f;
   }
 
-  const int n_spans = p.counts[qt];
-  const Span* spans = p.spans + (int64_t)qt * p.max_spans;
+  const int n_spans = p.counts[tile];
+  const Span* spans = p.spans + (int64_t)tile * p.max_spans;
 
   // tile iterator over the spans (block-uniform)
   int e = 0;
@@ -533,8 +540,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   for (int q = 0; q < QB; ++q) {
     const float l_tot = pair_sum(st[q].l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (row[q] < p.lq) {
-      __bf16* orow = p.o + ((int64_t)row[q] * p.H + h) * D;
+    if (row[q] < lq) {
+      __bf16* orow = odst + ((int64_t)row[q] * p.H + h) * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -546,8 +553,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
               make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
         }
       }
-      if (p.lse != nullptr && g == 0) {
-        p.lse[(int64_t)h * p.lq + row[q]] =
+      if (lse_dst != nullptr && g == 0) {
+        lse_dst[(int64_t)h * lq + row[q]] =
             l_tot > 0.0f ? (st[q].m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
       }
     }

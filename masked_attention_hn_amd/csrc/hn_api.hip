@@ -92,6 +92,7 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   const int lq = s->frames * P;
   pp->tile_q = sp ? HN_TILE : hn::attn_dense_rows();
   pp->n_qtiles = (int)ceil_div(lq, pp->tile_q);
+  pp->n_text_tiles = (int)ceil_div(tl, pp->tile_q);
   pp->lq = lq;
   pp->P = P;
   pp->head_tokens = c->head_tokens;
@@ -219,7 +220,7 @@ hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void*
 size_t hn_attn_workspace_size(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp) {
   hn::PlanParams pp;
   if (make_plan_params(c, s, sp, &pp) != HN_OK) return 0;
-  return hn::plan_bytes(pp.n_qtiles, pp.max_spans);
+  return hn::plan_bytes(pp.n_qtiles + pp.n_text_tiles, pp.max_spans);
 }
 
 hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
@@ -232,7 +233,7 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
   if (mode == HN_MASK_TILE_PLAN) {
     if (!plan) return fail(HN_ERR_NULL, "plan is NULL");
     if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return fail(HN_ERR_INVALID, "workspace not 16-byte aligned");
-    const size_t need = hn::plan_bytes(pp.n_qtiles, pp.max_spans);
+    const size_t need = hn::plan_bytes(pp.n_qtiles + pp.n_text_tiles, pp.max_spans);
     if (out_bytes < need)
       return fail(HN_ERR_WORKSPACE, "workspace of %zu bytes; %zu needed", out_bytes, need);
     hipError_t e = hn::launch_plan(pp, out, stream);
@@ -240,11 +241,21 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
     plan->dev = out;
     plan->tile_q = pp.tile_q;
     plan->n_qtiles = pp.n_qtiles;
+    plan->n_text_tiles = pp.n_text_tiles;
     plan->max_spans = pp.max_spans;
     plan->seg_index = s->index;
-    plan->frames_seen = c->frames_seen;
     plan->head_tokens = c->head_tokens;
+    plan->frames_seen = c->frames_seen;
     plan->sparse = pp.sparse;
+    plan->reserved0 = 0;
+    {
+      // text queries: every text row sees heads, ring, own head and own
+      // video; a tail row also sees its own tail
+      const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
+      int64_t pairs = (int64_t)pp.text_len * base;
+      for (int j = 0; j < s->num_actions; ++j) pairs += (int64_t)s->action_len[j] * s->action_len[j];
+      plan->visible_pairs_text = pairs;
+    }
     if (pp.sparse) {
       plan->visible_pairs = -1;
     } else {
@@ -262,8 +273,8 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
   }
   if (mode != HN_MASK_DENSE) return fail(HN_ERR_INVALID, "unknown mask mode %d", (int)mode);
   if (plan) return fail(HN_ERR_INVALID, "plan must be NULL in DENSE mode");
-  if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > pp.lq)
-    return fail(HN_ERR_INVALID, "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, pp.lq);
+  if (row0 < 0 || nrows < 0 || (int64_t)row0 + nrows > (int64_t)pp.lq + pp.text_len)
+    return fail(HN_ERR_INVALID, "rows [%d, %d) outside [0, %d)", row0, row0 + nrows, pp.lq + pp.text_len);
   if ((size_t)pp.max_spans * sizeof(hn::Span) > 64 * 1024)
     return fail(HN_ERR_UNSUPPORTED, "%d spans per tile exceed the dense expander's LDS", pp.max_spans);
   hn::DenseParams d;
@@ -284,8 +295,9 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
 }
 
 hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn_tile_plan* plan,
-                          const void* q_vid, const void* k_txt, const void* v_txt, const void* k_vid,
-                          const void* v_vid, void* o_vid, float* lse, float sm_scale, hipStream_t stream) {
+                          const void* q_vid, const void* q_txt, const void* k_txt, const void* v_txt,
+                          const void* k_vid, const void* v_vid, void* o_vid, void* o_txt, float* lse,
+                          float* lse_txt, float sm_scale, hipStream_t stream) {
   hn_status st = check_cache(c);
   if (st != HN_OK) return st;
   int64_t tl = 0;
@@ -298,10 +310,12 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   const int want_tile = plan->sparse ? HN_TILE : hn::attn_dense_rows();
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
       plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
-      plan->n_qtiles != (int)ceil_div(lq, want_tile))
+      plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile))
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
+  const bool text_q = q_txt != nullptr && tl > 0;
+  if (text_q && !o_txt) return fail(HN_ERR_NULL, "o_txt is NULL while q_txt is given");
   if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
   // the kernel addresses every source through 32-bit buffer offsets
   const int64_t tok_bytes = (int64_t)c->num_heads * HN_HEAD_DIM * 2;
@@ -314,10 +328,12 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   std::memset(&p, 0, sizeof(p));
   p.H = c->num_heads;
   p.lq = lq;
+  p.lq_txt = (int32_t)tl;
   p.n_qtiles = plan->n_qtiles;
+  p.n_tiles = plan->n_qtiles + (text_q ? plan->n_text_tiles : 0);
   p.tile_rows = plan->tile_q;
   p.max_spans = plan->max_spans;
-  p.n_tasks = p.H * p.n_qtiles;
+  p.n_tasks = p.H * p.n_tiles;
   p.tasks_per_xcd = (p.n_tasks + 7) / 8;
   p.head_cap = c->head_cap_tokens;
   p.ring_cap = c->window_frames * P;
@@ -325,8 +341,9 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.txt_len = (int32_t)tl;
   p.counts = static_cast<const int32_t*>(plan->dev);
   p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
-                                              hn::plan_counts_bytes(plan->n_qtiles));
+                                              hn::plan_counts_bytes(plan->n_qtiles + plan->n_text_tiles));
   p.q = static_cast<const __bf16*>(q_vid);
+  p.q_txt = text_q ? static_cast<const __bf16*>(q_txt) : nullptr;
   p.k_txt = static_cast<const __bf16*>(k_txt);
   p.v_txt = static_cast<const __bf16*>(v_txt);
   p.k_vid = static_cast<const __bf16*>(k_vid);
@@ -334,7 +351,9 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.heads_k = c->heads_k; p.heads_v = c->heads_v; p.heads_ks = c->heads_ks; p.heads_vs = c->heads_vs;
   p.ring_k = c->ring_k; p.ring_v = c->ring_v; p.ring_ks = c->ring_ks; p.ring_vs = c->ring_vs;
   p.o = static_cast<__bf16*>(o_vid);
+  p.o_txt = text_q ? static_cast<__bf16*>(o_txt) : nullptr;
   p.lse = lse;
+  p.lse_txt = text_q ? lse_txt : nullptr;
   hipError_t e = hn::launch_attn(p, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return ok();

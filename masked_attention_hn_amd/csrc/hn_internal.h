@@ -32,7 +32,8 @@ static_assert(sizeof(Span) == 32, "Span layout");
 
 // Everything the span builder needs; passed by value to kernels.
 struct PlanParams {
-  int32_t n_qtiles;
+  int32_t n_qtiles;      // video query tiles
+  int32_t n_text_tiles;  // text query tiles, after the video tiles
   int32_t tile_q;
   int32_t lq;            // F*P video queries
   int32_t P;
@@ -52,7 +53,6 @@ struct PlanParams {
   int32_t sparse;
   int32_t n_hist_tiles;
   int32_t n_own_tiles;
-  int32_t pad0;
   const int32_t* row_ptr;
   const int32_t* col;
 };
@@ -69,8 +69,10 @@ inline size_t plan_bytes(int n_qtiles, int max_spans) {
 
 struct AttnParams {
   int32_t H;
-  int32_t lq;
-  int32_t n_qtiles;
+  int32_t lq;            // video query rows
+  int32_t n_qtiles;      // video query tiles
+  int32_t n_tiles;       // tiles per head this launch covers (video, then text if any)
+  int32_t lq_txt;        // text query rows
   int32_t tile_rows;     // query rows per plan tile (selects the kernel instance)
   int32_t max_spans;
   int32_t n_tasks;
@@ -79,10 +81,10 @@ struct AttnParams {
   int32_t ring_cap;      // ring stride (tokens) per head = W*P
   float scale_log2;      // sm_scale * log2(e)
   int32_t txt_len;       // h + sum(a) text rows of the current segment
-  int32_t pad0;
   const int32_t* counts;
   const Span* spans;
   const __bf16* q;
+  const __bf16* q_txt;
   const __bf16* k_txt;
   const __bf16* v_txt;
   const __bf16* k_vid;
@@ -96,7 +98,9 @@ struct AttnParams {
   const float* ring_ks;
   const float* ring_vs;
   __bf16* o;
+  __bf16* o_txt;
   float* lse;
+  float* lse_txt;
 };
 
 struct AppendParams {

@@ -18,6 +18,12 @@
 // partial and carry their row range [f0*P, f1*P).  Adjacent spans of the same
 // source that are both full (or share a row range) are merged, so a dense plan
 // has at most 4 + m spans per tile.
+//
+// Text-query tiles (the segment's head and tail tokens as queries) follow the
+// video tiles.  Same segment-causal rule; their rows are text rows, tail j is
+// visible only to its own rows [off_j, off_j + a_j) and never to head rows,
+// and they attend densely (keep lists concern video query tiles): at most
+// 4 + m spans as well.
 #include <climits>
 
 #include "hn_internal.h"
@@ -68,7 +74,27 @@ __device__ void emit_ring_tile(SpanWriter& w, const PlanParams& p, int c) {
   }
 }
 
+// Spans of text-query tile tt (text rows [tt*tile_q, ...)).
+__device__ int build_text_spans(const PlanParams& p, int tt, Span* out) {
+  SpanWriter w;
+  w.out = out;
+  w.n = 0;
+  w.cap = p.max_spans;
+  w.R0 = tt * p.tile_q;
+  w.R1 = min(w.R0 + p.tile_q, p.text_len);
+  w.emit(SRC_HEADS, 0, p.head_tokens, 0, INT_MAX);
+  w.emit(SRC_RING, 0, p.ring_tokens, 0, INT_MAX);
+  w.emit(SRC_TXT, 0, p.head_len, 0, INT_MAX);
+  for (int j = 0; j < p.m; ++j) {
+    const int off = p.tail_off[j];
+    w.emit(SRC_TXT, off, off + p.tail_len[j], off, off + p.tail_len[j]);
+  }
+  w.emit(SRC_VID, 0, p.lq, 0, INT_MAX);
+  return w.n;
+}
+
 __device__ int build_spans(const PlanParams& p, int qt, Span* out) {
+  if (qt >= p.n_qtiles) return build_text_spans(p, qt - p.n_qtiles, out);
   SpanWriter w;
   w.out = out;
   w.n = 0;
@@ -124,7 +150,7 @@ __device__ int build_spans(const PlanParams& p, int qt, Span* out) {
 
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
   const int qt = blockIdx.x * 64 + threadIdx.x;
-  if (qt >= p.n_qtiles) return;
+  if (qt >= p.n_qtiles + p.n_text_tiles) return;
   counts[qt] = build_spans(p, qt, spans + (int64_t)qt * p.max_spans);
 }
 
@@ -151,10 +177,15 @@ __device__ int64_t canon_col(const DenseParams& d, int src, int k) {
 __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
   extern __shared__ Span sh_spans[];
   __shared__ int sh_n;
-  const int row = d.row0 + blockIdx.x;
+  // rows [0, lq) are video queries, rows [lq, lq + text_len) text queries;
+  // spans carry row ranges in the local rows of their query set
+  const int qrow = d.row0 + blockIdx.x;
+  const bool text = qrow >= d.plan.lq;
+  const int row = text ? qrow - d.plan.lq : qrow;
+  const int tile = text ? d.plan.n_qtiles + row / d.plan.tile_q : row / d.plan.tile_q;
   uint8_t* out = d.out + (int64_t)blockIdx.x * d.lk;
   for (int64_t c = threadIdx.x; c < d.lk; c += blockDim.x) out[c] = 0;
-  if (threadIdx.x == 0) sh_n = build_spans(d.plan, row / d.plan.tile_q, sh_spans);
+  if (threadIdx.x == 0) sh_n = build_spans(d.plan, tile, sh_spans);
   __syncthreads();
   const int n = sh_n;
   for (int e = 0; e < n; ++e) {
@@ -168,9 +199,9 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
 
 hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
-  Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) +
-                                        plan_counts_bytes(p.n_qtiles));
-  const int blocks = (p.n_qtiles + 63) / 64;
+  const int tiles = p.n_qtiles + p.n_text_tiles;
+  Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(tiles));
+  const int blocks = (tiles + 63) / 64;
   hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(64), 0, s, p, counts, spans);
   return hipGetLastError();
 }

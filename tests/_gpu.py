@@ -51,12 +51,20 @@ class Run:
         self.k_txt, self.v_txt = dev(d["k_txt"]), dev(d["v_txt"])
         self.k_vid, self.v_vid = dev(d["k_vid"]), dev(d["v_vid"])
         self.q = dev(data["q_vid"])
+        self.q_txt = dev(data["q_txt"]) if w.current.text_len > 0 else None
         self.sparse = sparse_of(w, data) if use_sparse else None
         self.plan = hn.build_plan(self.cache, self.seg, self.sparse)
 
     def attn(self, with_lse=True):
         out = hn.seg_attn(self.cache, self.seg, self.plan, self.q, self.k_txt, self.v_txt,
                           self.k_vid, self.v_vid, with_lse=with_lse)
+        torch.cuda.synchronize()
+        return out
+
+    def attn_joint(self):
+        """(o_vid, o_txt, lse_vid, lse_txt) of one call with both query sets."""
+        out = hn.seg_attn_joint(self.cache, self.seg, self.plan, self.q, self.q_txt, self.k_txt,
+                                self.v_txt, self.k_vid, self.v_vid)
         torch.cuda.synchronize()
         return out
 

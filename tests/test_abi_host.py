@@ -82,13 +82,14 @@ def test_workspace_sizes_and_plan_checks():
     c = fake_cache()
     s = seg_c()
     n = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
-    # counts padded to 256 bytes + one query tile x (4 + 2 tails) spans of 32 bytes
-    assert n == 256 + 1 * 6 * 32
+    # counts padded to 256 bytes + (one video + one text query tile) x (4 + 2 tails)
+    # spans of 32 bytes
+    assert n == 256 + 2 * 6 * 32
     bad = hn.hn_block_sparse(64, 64, 1, 0, FAKE, FAKE)
     assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad)) == 0
     sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
     n_sp = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(sp))
-    assert n_sp == 256 + (4 + 2 + 0 + 1 + 1) * 32
+    assert n_sp == 256 + 2 * (4 + 2 + 0 + 1 + 1) * 32
     plan = hn.hn_tile_plan()
     build = hn._lib.hn_attn_mask_build
     assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n - 1,
@@ -99,8 +100,8 @@ def test_workspace_sizes_and_plan_checks():
                  None) == hn.HN_ERR_NULL
     assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * 1000,
                  ctypes.byref(plan), None) == hn.HN_ERR_INVALID                # plan in DENSE
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 40, 9, FAKE, 10 ** 6, None,
-                 None) == hn.HN_ERR_INVALID                                    # rows past F*P
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 40, 41, FAKE, 10 ** 6, None,
+                 None) == hn.HN_ERR_INVALID                    # rows past F*P + h + sum(a)
     lk = 0 + 0 + 32 + 48
     assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * lk - 1, None,
                  None) == hn.HN_ERR_WORKSPACE
@@ -111,23 +112,29 @@ def test_workspace_sizes_and_plan_checks():
 def test_attention_rejects_stale_plan():
     c = fake_cache()
     s = seg_c()
-    plan = hn.hn_tile_plan(FAKE, 128, 1, 6, 0, 0, 0, 0, -1)   # 128-row query tiles
+    plan = hn.hn_tile_plan(dev=FAKE, tile_q=128, n_qtiles=1, n_text_tiles=1, max_spans=6,
+                           visible_pairs=-1)          # 128-row query tiles
     fwd = hn._lib.hn_seg_attn_fwd
-    args = [FAKE] * 6  # q, k_txt, v_txt, k_vid, v_vid, o
+    q = [FAKE, None]                # q_vid, q_txt
+    kv = [FAKE] * 4                 # k_txt, v_txt, k_vid, v_vid
+    out = [FAKE, None, None, None]  # o_vid, o_txt, lse, lse_txt
+    call = lambda seg, pl, qq=q, oo=out, scale=0.1: fwd(ctypes.byref(c), ctypes.byref(seg.c), pl,
+                                                        *qq, *kv, *oo, scale, None)
     plan.frames_seen = 24          # built for another cache state
-    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None, 0.1,
-               None) == hn.HN_ERR_ORDER
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
     plan.frames_seen = 0
     plan.seg_index = 1
-    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None, 0.1,
-               None) == hn.HN_ERR_ORDER
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
     plan.seg_index = 0
-    assert fwd(ctypes.byref(c), ctypes.byref(s.c), None, *args, None, 0.1, None) == hn.HN_ERR_NULL
-    assert fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), *args, None,
-               float("nan"), None) == hn.HN_ERR_INVALID
+    plan.n_text_tiles = 2          # text tiles of another layout
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.n_text_tiles = 1
+    assert call(s, None) == hn.HN_ERR_NULL
+    assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID
+    # text queries without their output
+    assert call(s, ctypes.byref(plan), qq=[FAKE, FAKE]) == hn.HN_ERR_NULL
     s2 = seg_c(index=1)
-    assert fwd(ctypes.byref(c), ctypes.byref(s2.c), ctypes.byref(plan), *args, None, 0.1,
-               None) == hn.HN_ERR_ORDER
+    assert call(s2, ctypes.byref(plan)) == hn.HN_ERR_ORDER
 
 
 def test_cache_sizes():
