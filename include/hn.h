@@ -187,7 +187,16 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
  * It may be reused by every attention call of the segment (all blocks and
  * denoising steps with the same keep list).  Tiles 0 .. n_qtiles-1 cover
  * the video queries, tiles n_qtiles .. n_qtiles+n_text_tiles-1 the text
- * queries (head and tails). */
+ * queries (head and tails).
+ * Split-KV: when (heads x video query tiles) would leave the GPU's block
+ * slots (2 per compute unit) poorly filled, every query tile's keys are
+ * split into n_splits contiguous ranges that run as separate blocks; each
+ * writes a partial result into the workspace and a merge kernel combines
+ * them (one softmax, exactly as without the split up to rounding).  The
+ * split count comes from the device's compute-unit count and the layout;
+ * HN_ATTN_SPLITS=n in the environment forces n (1..16).  With n_splits > 1
+ * attention calls that share one plan workspace must not overlap in time
+ * (same stream, or ordered), since they write its partial area. */
 typedef struct hn_tile_plan {
   const void* dev;            /* = the workspace the plan was written to */
   int32_t tile_q;             /* query rows per plan tile */
@@ -198,12 +207,14 @@ typedef struct hn_tile_plan {
   int32_t head_tokens;
   int64_t frames_seen;
   int32_t sparse;             /* 1 if a keep list was merged */
-  int32_t reserved0;
+  int32_t n_splits;           /* key splits per query tile (split-KV), 1 .. 16 */
   int64_t visible_pairs;      /* unmasked (video query, key) pairs per head; -1 if sparse */
   int64_t visible_pairs_text; /* unmasked (text query, key) pairs per head */
 } hn_tile_plan;
 
-/* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments). */
+/* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments): the span
+ * lists, plus, with split-KV, H x tiles x splits x tile_q x (128 + 1) floats
+ * of partial results. */
 size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg,
                               const hn_block_sparse* sparse);
 

@@ -422,7 +422,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   const int task = (blockIdx.x & 7) * p.tasks_per_xcd + (blockIdx.x >> 3);
   if (task >= p.n_tasks) return;  // whole block leaves before any barrier
   const int h = task / p.n_tiles;
-  const int tile = task - h * p.n_tiles;
+  const int vt = task - h * p.n_tiles;  // virtual tile: (query tile, key split), split fastest
+  const int tile = vt / p.n_splits;
   // plan tiles: video query tiles, then text query tiles (own head and tails)
   const bool text = tile >= p.n_qtiles;
   const int qt = text ? tile - p.n_qtiles : tile;  // tile within its query set
@@ -464,8 +465,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     st[q].l = 0.0f;
   }
 
-  const int n_spans = p.counts[tile];
-  const Span* spans = p.spans + (int64_t)tile * p.max_spans;
+  const int n_spans = p.counts[vt];
+  const Span* spans = p.spans + (int64_t)vt * p.max_spans;
 
   // tile iterator over the spans (block-uniform)
   int e = 0;
@@ -535,29 +536,86 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     step(stage1, stage0);
   }
 
-  // epilogue: O = acc / l, lse = (m + log2 l) * ln 2
+  // epilogue: O = acc / l, lse = (m + log2 l) * ln 2; with key splits the
+  // normalized fp32 O and the lse of this split go to the partial buffers
 #pragma unroll
   for (int q = 0; q < QB; ++q) {
     const float l_tot = pair_sum(st[q].l);
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
-    if (row[q] < lq) {
-      __bf16* orow = odst + ((int64_t)row[q] * p.H + h) * D;
+    const float lse_v = l_tot > 0.0f ? (st[q].m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+    if (row[q] >= lq) continue;
+    if (p.n_splits > 1) {
+      const int64_t prow = ((int64_t)h * p.n_vt + vt) * C::ROWS + (row[q] - qt * C::ROWS);
+      float* orow = p.part_o + prow * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int d0 = 32 * c + 8 * r + 4 * g;
-          const bf16x2 lo = {(__bf16)(acc[q][c][4 * r + 0] * inv), (__bf16)(acc[q][c][4 * r + 1] * inv)};
-          const bf16x2 hi = {(__bf16)(acc[q][c][4 * r + 2] * inv), (__bf16)(acc[q][c][4 * r + 3] * inv)};
-          *reinterpret_cast<uint2*>(orow + d0) =
-              make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+          *reinterpret_cast<float4*>(orow + d0) =
+              make_float4(acc[q][c][4 * r + 0] * inv, acc[q][c][4 * r + 1] * inv,
+                          acc[q][c][4 * r + 2] * inv, acc[q][c][4 * r + 3] * inv);
         }
       }
-      if (lse_dst != nullptr && g == 0) {
-        lse_dst[(int64_t)h * lq + row[q]] =
-            l_tot > 0.0f ? (st[q].m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+      if (g == 0) p.part_lse[prow] = lse_v;
+      continue;
+    }
+    __bf16* orow = odst + ((int64_t)row[q] * p.H + h) * D;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * c + 8 * r + 4 * g;
+        const bf16x2 lo = {(__bf16)(acc[q][c][4 * r + 0] * inv), (__bf16)(acc[q][c][4 * r + 1] * inv)};
+        const bf16x2 hi = {(__bf16)(acc[q][c][4 * r + 2] * inv), (__bf16)(acc[q][c][4 * r + 3] * inv)};
+        *reinterpret_cast<uint2*>(orow + d0) =
+            make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
       }
     }
+    if (lse_dst != nullptr && g == 0) lse_dst[(int64_t)h * lq + row[q]] = lse_v;
+  }
+}
+
+// Split-KV merge: for every (head, query tile) the n_splits partial results
+// (normalized O in fp32, lse) of the same rows are combined exactly as one
+// softmax over the union of their keys: with M = max_s lse_s and
+// w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
+// lse = M + log(sum_s w_s); rows no split saw (all lse = -inf) get O = 0.
+// Block = one (head, tile); lane group of 32 covers one 128-wide row with
+// float4 loads, 8 rows in flight per pass.
+__global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
+  const int h = blockIdx.x / p.n_tiles;
+  const int t = blockIdx.x - h * p.n_tiles;
+  const bool text = t >= p.n_qtiles;
+  const int qt = text ? t - p.n_qtiles : t;
+  const int lq = text ? p.lq_txt : p.lq;
+  __bf16* out = text ? p.o_txt : p.o;
+  float* lse_out = text ? p.lse_txt : p.lse;
+  const int d4 = threadIdx.x & 31;
+  for (int rl = threadIdx.x >> 5; rl < p.tile_rows; rl += 8) {
+    const int row = qt * p.tile_rows + rl;
+    if (row >= lq) break;
+    const int64_t base = ((int64_t)h * p.n_vt + (int64_t)t * p.n_splits) * p.tile_rows + rl;
+    float m = -INFINITY;
+    for (int sp = 0; sp < p.n_splits; ++sp) m = fmaxf(m, p.part_lse[base + (int64_t)sp * p.tile_rows]);
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    float wsum = 0.0f;
+    if (m != -INFINITY) {
+      for (int sp = 0; sp < p.n_splits; ++sp) {
+        const int64_t pr = base + (int64_t)sp * p.tile_rows;
+        const float w = expf(p.part_lse[pr] - m);
+        const float4 v = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * d4);
+        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+        wsum += w;
+      }
+    }
+    const float inv = wsum > 0.0f ? 1.0f / wsum : 0.0f;
+    const bf16x2 lo = {(__bf16)(acc.x * inv), (__bf16)(acc.y * inv)};
+    const bf16x2 hi = {(__bf16)(acc.z * inv), (__bf16)(acc.w * inv)};
+    *reinterpret_cast<uint2*>(out + ((int64_t)row * p.H + h) * D + 4 * d4) =
+        make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+    if (lse_out != nullptr && d4 == 0)
+      lse_out[(int64_t)h * lq + row] = wsum > 0.0f ? m + logf(wsum) : -INFINITY;
   }
 }
 
@@ -593,6 +651,13 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeParams& p, hipStream_t s) {
+  const int64_t blocks = (int64_t)p.H * p.n_tiles;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "hn_internal.h"
@@ -80,6 +81,39 @@ int kept_frames(const hn_kv_cache* c) {
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Compute units of the current device (256 on MI355X; also the answer when
+// no device is visible, so that sizes computed on a host agree).
+int device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    return 256;
+  return n;
+}
+
+// Key splits per query tile (split-KV).  Measured on MI355X, splitting does
+// not pay once the grid has at least one block per compute unit: a CU
+// holding one 4-wave block runs it nearly as fast as it runs two, and the
+// fp32 partial results plus the merge cost more than the better fill (the
+// 2-head share of the 1280x704 steady state, 414 blocks on 256 CUs: 1.54 ms
+// unsplit, 1.73 / 1.59 / 1.61 / 1.56 ms with 2 / 3 / 4 / 8 splits).  So only
+// grids with fewer blocks than CUs are split, to about two blocks per CU and
+// no fewer than 1024 keys per split.  HN_ATTN_SPLITS=n in the environment
+// forces n (tuning and tests).
+int choose_splits(int H, int n_qtiles, int64_t keys_per_tile) {
+  if (const char* e = std::getenv("HN_ATTN_SPLITS")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= HN_MAX_SPLITS) return v;
+  }
+  const int64_t cus = device_cus();
+  const int64_t tasks = (int64_t)H * n_qtiles;
+  if (tasks <= 0 || tasks >= cus) return 1;
+  int64_t sp = ceil_div(2 * cus, tasks);
+  sp = std::min<int64_t>(sp, keys_per_tile / 1024);
+  sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
+  return (int)std::max<int64_t>(sp, 1);
+}
+
 // Plan parameters for the current state; validates the keep list.
 hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
                            hn::PlanParams* pp) {
@@ -113,6 +147,13 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   }
   pp->n_hist_tiles = (int)ceil_div(pp->ring_tokens, HN_TILE);
   pp->n_own_tiles = (int)ceil_div(lq, HN_TILE);
+  {
+    // keys a video query tile visits (a keep list keeps about its share of video)
+    int64_t keys = (int64_t)pp->head_tokens + tl;
+    int64_t video = (int64_t)pp->ring_tokens + lq;
+    if (sp && sp->row_ptr && pp->n_qtiles > 0) video = video / 4;
+    pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video);
+  }
   int max_spans = 4 + s->num_actions;
   if (sp) {
     if (sp->tile_q != HN_TILE || sp->tile_k != HN_TILE)
@@ -129,6 +170,12 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   }
   pp->max_spans = max_spans;
   return HN_OK;
+}
+
+int plan_vt(const hn::PlanParams& pp) { return (pp.n_qtiles + pp.n_text_tiles) * pp.n_splits; }
+
+size_t plan_ws_bytes(const hn_kv_cache* c, const hn::PlanParams& pp) {
+  return hn::plan_bytes(c->num_heads, plan_vt(pp), pp.max_spans, pp.tile_q, pp.n_splits);
 }
 
 hn_status hip_fail(hipError_t e, const char* what) {
@@ -220,7 +267,7 @@ hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void*
 size_t hn_attn_workspace_size(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp) {
   hn::PlanParams pp;
   if (make_plan_params(c, s, sp, &pp) != HN_OK) return 0;
-  return hn::plan_bytes(pp.n_qtiles + pp.n_text_tiles, pp.max_spans);
+  return plan_ws_bytes(c, pp);
 }
 
 hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
@@ -233,7 +280,7 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
   if (mode == HN_MASK_TILE_PLAN) {
     if (!plan) return fail(HN_ERR_NULL, "plan is NULL");
     if (reinterpret_cast<uintptr_t>(out) % 16 != 0) return fail(HN_ERR_INVALID, "workspace not 16-byte aligned");
-    const size_t need = hn::plan_bytes(pp.n_qtiles + pp.n_text_tiles, pp.max_spans);
+    const size_t need = plan_ws_bytes(c, pp);
     if (out_bytes < need)
       return fail(HN_ERR_WORKSPACE, "workspace of %zu bytes; %zu needed", out_bytes, need);
     hipError_t e = hn::launch_plan(pp, out, stream);
@@ -247,7 +294,7 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
     plan->head_tokens = c->head_tokens;
     plan->frames_seen = c->frames_seen;
     plan->sparse = pp.sparse;
-    plan->reserved0 = 0;
+    plan->n_splits = pp.n_splits;
     {
       // text queries: every text row sees heads, ring, own head and own
       // video; a tail row also sees its own tail
@@ -310,7 +357,8 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   const int want_tile = plan->sparse ? HN_TILE : hn::attn_dense_rows();
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
       plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
-      plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile))
+      plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile) ||
+      plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS)
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
@@ -330,7 +378,9 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.lq = lq;
   p.lq_txt = (int32_t)tl;
   p.n_qtiles = plan->n_qtiles;
-  p.n_tiles = plan->n_qtiles + (text_q ? plan->n_text_tiles : 0);
+  p.n_splits = plan->n_splits;
+  p.n_vt = (plan->n_qtiles + plan->n_text_tiles) * plan->n_splits;
+  p.n_tiles = (plan->n_qtiles + (text_q ? plan->n_text_tiles : 0)) * plan->n_splits;
   p.tile_rows = plan->tile_q;
   p.max_spans = plan->max_spans;
   p.n_tasks = p.H * p.n_tiles;
@@ -341,7 +391,13 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.txt_len = (int32_t)tl;
   p.counts = static_cast<const int32_t*>(plan->dev);
   p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
-                                              hn::plan_counts_bytes(plan->n_qtiles + plan->n_text_tiles));
+                                              hn::plan_counts_bytes(p.n_vt));
+  if (p.n_splits > 1) {
+    char* base = const_cast<char*>(static_cast<const char*>(plan->dev)) +
+                 hn::align256(hn::plan_spans_bytes(p.n_vt, plan->max_spans));
+    p.part_o = reinterpret_cast<float*>(base);
+    p.part_lse = reinterpret_cast<float*>(base + hn::plan_partial_o_bytes(p.H, p.n_vt, plan->tile_q));
+  }
   p.q = static_cast<const __bf16*>(q_vid);
   p.q_txt = text_q ? static_cast<const __bf16*>(q_txt) : nullptr;
   p.k_txt = static_cast<const __bf16*>(k_txt);
@@ -356,6 +412,26 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.lse_txt = text_q ? lse_txt : nullptr;
   hipError_t e = hn::launch_attn(p, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (p.n_splits > 1) {
+    hn::MergeParams m;
+    std::memset(&m, 0, sizeof(m));
+    m.H = p.H;
+    m.n_splits = p.n_splits;
+    m.n_vt = p.n_vt;
+    m.tile_rows = plan->tile_q;
+    m.n_qtiles = plan->n_qtiles;
+    m.n_tiles = p.n_tiles / p.n_splits;
+    m.lq = lq;
+    m.lq_txt = (int32_t)tl;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.o = p.o;
+    m.o_txt = p.o_txt;
+    m.lse = p.lse;
+    m.lse_txt = p.lse_txt;
+    e = hn::launch_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "split merge launch");
+  }
   return ok();
 }
 

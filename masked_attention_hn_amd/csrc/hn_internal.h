@@ -10,6 +10,7 @@ namespace hn {
 
 constexpr int D = HN_HEAD_DIM;
 constexpr int TILE = HN_TILE;
+#define HN_MAX_SPLITS 16  // key splits per query tile (split-KV)
 
 // Key sources an attention span can come from.
 enum Src : int32_t {
@@ -34,6 +35,7 @@ static_assert(sizeof(Span) == 32, "Span layout");
 struct PlanParams {
   int32_t n_qtiles;      // video query tiles
   int32_t n_text_tiles;  // text query tiles, after the video tiles
+  int32_t n_splits;      // key-range splits per query tile (split-KV); 1 = none
   int32_t tile_q;
   int32_t lq;            // F*P video queries
   int32_t P;
@@ -57,21 +59,34 @@ struct PlanParams {
   const int32_t* col;
 };
 
-// Workspace layout of a tile plan: int32 count[n_qtiles] padded to 256 bytes,
-// then Span spans[n_qtiles][max_spans].
-inline size_t plan_counts_bytes(int n_qtiles) {
-  size_t b = (size_t)n_qtiles * sizeof(int32_t);
-  return (b + 255) & ~(size_t)255;
+// Workspace layout of a tile plan over n_vt virtual tiles (query tile x key
+// split, split fastest): int32 count[n_vt] padded to 256 bytes, then
+// Span spans[n_vt][max_spans]; with splits, then (256-byte aligned) the
+// partial results float o[H][n_vt][rows][D] and float lse[H][n_vt][rows].
+inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+inline size_t plan_counts_bytes(int n_vt) { return align256((size_t)n_vt * sizeof(int32_t)); }
+inline size_t plan_spans_bytes(int n_vt, int max_spans) {
+  return plan_counts_bytes(n_vt) + (size_t)n_vt * max_spans * sizeof(Span);
 }
-inline size_t plan_bytes(int n_qtiles, int max_spans) {
-  return plan_counts_bytes(n_qtiles) + (size_t)n_qtiles * max_spans * sizeof(Span);
+inline size_t plan_partial_o_bytes(int H, int n_vt, int rows) {
+  return align256((size_t)H * n_vt * rows * D * sizeof(float));
+}
+inline size_t plan_partial_lse_bytes(int H, int n_vt, int rows) {
+  return align256((size_t)H * n_vt * rows * sizeof(float));
+}
+inline size_t plan_bytes(int H, int n_vt, int max_spans, int rows, int n_splits) {
+  size_t b = align256(plan_spans_bytes(n_vt, max_spans));
+  if (n_splits > 1) b += plan_partial_o_bytes(H, n_vt, rows) + plan_partial_lse_bytes(H, n_vt, rows);
+  return b;
 }
 
 struct AttnParams {
   int32_t H;
   int32_t lq;            // video query rows
   int32_t n_qtiles;      // video query tiles
-  int32_t n_tiles;       // tiles per head this launch covers (video, then text if any)
+  int32_t n_tiles;       // virtual tiles per head this launch covers (video, then text if any)
+  int32_t n_splits;      // key splits per query tile; > 1: write partials, merge after
+  int32_t n_vt;          // virtual tiles per head in the plan (partial-buffer stride)
   int32_t lq_txt;        // text query rows
   int32_t tile_rows;     // query rows per plan tile (selects the kernel instance)
   int32_t max_spans;
@@ -97,6 +112,25 @@ struct AttnParams {
   const int8_t* ring_v;
   const float* ring_ks;
   const float* ring_vs;
+  __bf16* o;
+  __bf16* o_txt;
+  float* lse;
+  float* lse_txt;
+  float* part_o;         // [H][n_vt][tile_rows][D] when n_splits > 1
+  float* part_lse;       // [H][n_vt][tile_rows]
+};
+
+// Merge of split-KV partials into the final O (bf16) and lse.
+struct MergeParams {
+  int32_t H;
+  int32_t n_splits;
+  int32_t n_vt;          // virtual tiles per head in the plan
+  int32_t tile_rows;
+  int32_t n_qtiles;      // video query tiles
+  int32_t n_tiles;       // query tiles merged (video, then text if any)
+  int32_t lq, lq_txt;
+  const float* part_o;
+  const float* part_lse;
   __bf16* o;
   __bf16* o_txt;
   float* lse;
@@ -147,5 +181,6 @@ hipError_t launch_quant_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s);
 hipError_t launch_dense(const DenseParams& p, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
+hipError_t launch_merge(const MergeParams& p, hipStream_t s);
 
 }  // namespace hn

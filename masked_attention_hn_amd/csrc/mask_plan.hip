@@ -24,6 +24,12 @@
 // visible only to its own rows [off_j, off_j + a_j) and never to head rows,
 // and they attend densely (keep lists concern video query tiles): at most
 // 4 + m spans as well.
+//
+// Split-KV: with n_splits > 1 every query tile becomes n_splits virtual tiles
+// (split fastest), each the same span list clipped to one contiguous range
+// of its keys in visiting order, with range boundaries on multiples of 64
+// keys; the attention kernel writes partial results for each and a merge
+// kernel combines them.
 #include <climits>
 
 #include "hn_internal.h"
@@ -93,7 +99,8 @@ __device__ int build_text_spans(const PlanParams& p, int tt, Span* out) {
   return w.n;
 }
 
-__device__ int build_spans(const PlanParams& p, int qt, Span* out) {
+// Full span list of query tile qt (video tiles, then text tiles).
+__device__ int build_tile_spans(const PlanParams& p, int qt, Span* out) {
   if (qt >= p.n_qtiles) return build_text_spans(p, qt - p.n_qtiles, out);
   SpanWriter w;
   w.out = out;
@@ -148,10 +155,44 @@ __device__ int build_spans(const PlanParams& p, int qt, Span* out) {
   return w.n;
 }
 
+// Key position where split i of n begins (multiples of 64 keys).
+__device__ int64_t split_bound(int64_t total, int i, int n) {
+  if (i >= n) return total;
+  return (total * i / n) & ~(int64_t)63;
+}
+
+// Span list of virtual tile vt = (query tile, key split).
+__device__ int build_spans(const PlanParams& p, int vt, Span* out) {
+  const int qt = vt / p.n_splits;
+  const int split = vt - qt * p.n_splits;
+  const int n = build_tile_spans(p, qt, out);
+  if (p.n_splits == 1) return n;
+  int64_t total = 0;
+  for (int i = 0; i < n; ++i) total += out[i].k1 - out[i].k0;
+  const int64_t a = split_bound(total, split, p.n_splits);
+  const int64_t b = split_bound(total, split + 1, p.n_splits);
+  // clip in place (entry m <= i is written only after entry i was read)
+  int m = 0;
+  int64_t pos = 0;
+  for (int i = 0; i < n; ++i) {
+    Span sp = out[i];
+    const int64_t len = sp.k1 - sp.k0;
+    const int64_t lo = a > pos ? a : pos;
+    const int64_t hi = b < pos + len ? b : pos + len;
+    if (lo < hi) {
+      sp.k0 += (int)(lo - pos);
+      sp.k1 = sp.k0 + (int)(hi - lo);
+      out[m++] = sp;
+    }
+    pos += len;
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
-  const int qt = blockIdx.x * 64 + threadIdx.x;
-  if (qt >= p.n_qtiles + p.n_text_tiles) return;
-  counts[qt] = build_spans(p, qt, spans + (int64_t)qt * p.max_spans);
+  const int vt = blockIdx.x * 64 + threadIdx.x;
+  if (vt >= (p.n_qtiles + p.n_text_tiles) * p.n_splits) return;
+  counts[vt] = build_spans(p, vt, spans + (int64_t)vt * p.max_spans);
 }
 
 // Canonical column of key k of a source (see hn.h, DENSE mode).
@@ -185,7 +226,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
   const int tile = text ? d.plan.n_qtiles + row / d.plan.tile_q : row / d.plan.tile_q;
   uint8_t* out = d.out + (int64_t)blockIdx.x * d.lk;
   for (int64_t c = threadIdx.x; c < d.lk; c += blockDim.x) out[c] = 0;
-  if (threadIdx.x == 0) sh_n = build_spans(d.plan, tile, sh_spans);
+  if (threadIdx.x == 0) sh_n = build_tile_spans(d.plan, tile, sh_spans);
   __syncthreads();
   const int n = sh_n;
   for (int e = 0; e < n; ++e) {
@@ -199,9 +240,9 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
 
 hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
-  const int tiles = p.n_qtiles + p.n_text_tiles;
-  Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(tiles));
-  const int blocks = (tiles + 63) / 64;
+  const int n_vt = (p.n_qtiles + p.n_text_tiles) * p.n_splits;
+  Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(n_vt));
+  const int blocks = (n_vt + 63) / 64;
   hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(64), 0, s, p, counts, spans);
   return hipGetLastError();
 }

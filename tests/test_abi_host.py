@@ -83,13 +83,14 @@ def test_workspace_sizes_and_plan_checks():
     s = seg_c()
     n = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
     # counts padded to 256 bytes + (one video + one text query tile) x (4 + 2 tails)
-    # spans of 32 bytes
-    assert n == 256 + 2 * 6 * 32
+    # spans of 32 bytes, padded to 256 bytes (4 query tiles of 2 heads: no key split)
+    assert n == 256 + 512
+    assert 256 + 2 * 6 * 32 <= n
     bad = hn.hn_block_sparse(64, 64, 1, 0, FAKE, FAKE)
     assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad)) == 0
     sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
     n_sp = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(sp))
-    assert n_sp == 256 + 2 * (4 + 2 + 0 + 1 + 1) * 32
+    assert n_sp == 256 + 2 * (4 + 2 + 0 + 1 + 1) * 32   # already a multiple of 256
     plan = hn.hn_tile_plan()
     build = hn._lib.hn_attn_mask_build
     assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n - 1,
@@ -113,7 +114,7 @@ def test_attention_rejects_stale_plan():
     c = fake_cache()
     s = seg_c()
     plan = hn.hn_tile_plan(dev=FAKE, tile_q=128, n_qtiles=1, n_text_tiles=1, max_spans=6,
-                           visible_pairs=-1)          # 128-row query tiles
+                           n_splits=1, visible_pairs=-1)          # 128-row query tiles
     fwd = hn._lib.hn_seg_attn_fwd
     q = [FAKE, None]                # q_vid, q_txt
     kv = [FAKE] * 4                 # k_txt, v_txt, k_vid, v_vid
@@ -129,6 +130,9 @@ def test_attention_rejects_stale_plan():
     plan.n_text_tiles = 2          # text tiles of another layout
     assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
     plan.n_text_tiles = 1
+    plan.n_splits = 0              # not a plan the builder writes
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.n_splits = 1
     assert call(s, None) == hn.HN_ERR_NULL
     assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID
     # text queries without their output
@@ -143,3 +147,43 @@ def test_cache_sizes():
     assert hb == 16 * 2304 * 128 and hsb == 16 * 2304 * 4
     with pytest.raises(hn.HNError):
         hn.hn_kv_cache_sizes(0, 18, 880, 0)
+
+
+def test_split_count_forced_and_sized(monkeypatch):
+    """HN_ATTN_SPLITS forces the key split; the workspace then also holds the
+    partial results: H x virtual tiles x 128 rows x (128 + 1) floats."""
+    c = fake_cache()
+    s = seg_c()
+    n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    monkeypatch.setenv("HN_ATTN_SPLITS", "3")
+    n3 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    vt = 2 * 3                                 # (video + text tile) x 3 splits
+    spans = -(-(256 + vt * 6 * 32) // 256) * 256
+    o = -(-(2 * vt * 128 * 128 * 4) // 256) * 256
+    lse = -(-(2 * vt * 128 * 4) // 256) * 256
+    assert n3 == spans + o + lse and n3 > n1
+    monkeypatch.setenv("HN_ATTN_SPLITS", "99")  # out of range: automatic choice
+    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None) == n1
+
+
+def test_automatic_split_only_for_small_grids(monkeypatch):
+    """Without a device (256 compute units assumed) a grid of at least 256
+    blocks is not split; a 1-head layout with 2 query tiles of long key lists
+    is split to about two blocks per CU, capped at 16 and at 1024 keys per split."""
+    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
+    plan_sizes = {}
+    for H, P, frames, W_ in ((16, 390, 30, 1), (1, 128, 2, 200)):
+        c = fake_cache(H=H, P=P, W=W_)
+        c.frames_seen = W_          # a full ring of history
+        seg = hn.SegLayout(0, frames, P, 16, [], [], [])
+        c.segments = 0
+        plan_sizes[H] = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+    # 16 heads x 92 tiles: spans only (no partial results)
+    n_vt = 92 + 1
+    assert plan_sizes[16] == -(-(-(-n_vt * 4 // 256) * 256 + n_vt * 4 * 32) // 256) * 256
+    # 1 head x 2 video tiles (+1 text tile): ring 25,600 + 16 + 256 keys -> 16 splits
+    n_vt = (2 + 1) * 16
+    spans = -(-(-(-n_vt * 4 // 256) * 256 + n_vt * 4 * 32) // 256) * 256
+    o = -(-(n_vt * 128 * 128 * 4) // 256) * 256
+    lse = -(-(n_vt * 128 * 4) // 256) * 256
+    assert plan_sizes[1] == spans + o + lse
