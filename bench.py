@@ -255,6 +255,43 @@ def main():
 
     traffic = counter_traffic(args.workload)
 
+    # history archive: evict (device -> pinned host) the frames the append of
+    # this segment pushes out of the window, append, then rewind (host ->
+    # device) to the state before it; repeated, each copy timed on the stream
+    archive = None
+    if w.window is not None and saved[0] >= w.window:
+        P = w.current.tokens_per_frame
+        ar = hn.KVArchive(w.heads, P, saved[0] + w.current.frames)
+        n_ar = 6
+        ed = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ar)]
+        eh = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n_ar)]
+        for i in range(n_ar):
+            cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
+            ar.c.frames = 0
+            ed[i][0].record(stream)
+            hn.hn_kv_archive_evict(cache, seg, ar)
+            ed[i][1].record(stream)
+            hn.hn_kv_quant_append(cache, seg, k_txt, v_txt, k_vid, v_vid)
+            eh[i][0].record(stream)
+            hn.hn_kv_cache_rewind(cache, ar, *saved)
+            eh[i][1].record(stream)
+        torch.cuda.synchronize()
+        n_frames = min(w.current.frames, w.window)
+        ar_bytes = n_frames * P * w.heads * (2 * 128 + 2 * 4)
+        d2h = sorted(a.elapsed_time(b) for a, b in ed)[n_ar // 2]
+        h2d = sorted(a.elapsed_time(b) for a, b in eh)[n_ar // 2]
+        archive = {
+            "what": "history frames leaving the window: device -> pinned host on append, "
+                    "host -> device on rewind (median of 6)",
+            "frames": n_frames,
+            "bytes": ar_bytes,
+            "d2h_ms": round(d2h, 4),
+            "d2h_GBps": round(ar_bytes / (d2h * 1e-3) / 1e9, 2),
+            "h2d_ms": round(h2d, 4),
+            "h2d_GBps": round(ar_bytes / (h2d * 1e-3) / 1e9, 2),
+        }
+        cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
+
     # the same call with the segment's text queries added (one launch for both)
     joint = None
     if w.current.text_len > 0:
@@ -326,6 +363,7 @@ def main():
             "avg_launch_ms": round(attn_avg, 4),
         },
         "joint": joint,
+        "archive": archive,
         "append": {
             "kernel": "quant_append_kernel",
             "bound": "hbm",

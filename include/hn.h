@@ -160,6 +160,62 @@ hn_status hn_kv_quant_append(hn_kv_cache* cache, const hn_seg_layout* seg,
                              const void* k_vid, const void* v_vid,
                              hipStream_t stream);
 
+/* Host archive of history frames that left the GPU window.
+ *
+ * The single-GPU configuration keeps a window of W history frames on the GPU
+ * and archives earlier history to CPU memory ([H] configuration table,
+ * history row; [T] "单卡 4090 怎么做到的", second technique).  The archive holds,
+ * in global frame order, the INT8 codes and scales of every frame the ring
+ * gave up, exactly as the ring held them, so that hn_kv_cache_rewind can put
+ * them back.  Frames a single segment longer than W drops at once were never
+ * in the ring and are not archived.
+ *
+ * Buffers are host memory allocated by the caller, pinned (hipHostMalloc) so
+ * that the copies run asynchronously on the stream; head-major like the ring:
+ *   k, v   int8 [H][cap_frames*P][D]   archived frame i, token t at row i*P+t
+ *   ks, vs fp32 [H][cap_frames*P]
+ * Archived frame i is global latent frame first_frame + i.  The counters are
+ * host-side; zero them for a new video.
+ */
+typedef struct hn_kv_archive {
+  int8_t* k;
+  int8_t* v;
+  float* ks;
+  float* vs;
+  int32_t cap_frames;         /* capacity in latent frames */
+  int32_t reserved0;
+  int64_t first_frame;        /* global frame of archived frame 0 */
+  int64_t frames;             /* frames held */
+} hn_kv_archive;
+
+/* Enqueue device-to-host copies of the ring frames that
+ * hn_kv_quant_append(cache, seg, ...) is about to overwrite: appending F
+ * frames after frames_seen = fs with window W evicts global frames
+ * [fs - min(fs, W), max(that, min(fs, fs + F - min(fs + F, W)))).  Call it
+ * right before that append, on the same stream (or one ordered before it);
+ * the copies finish before the append's kernel starts overwriting.  Appends
+ * archive->frames; the first eviction into an empty archive sets
+ * first_frame.  Errors: HN_ERR_ORDER if seg->index != cache->segments or the
+ * frames do not continue the archive; HN_ERR_CAPACITY if they do not fit
+ * (nothing enqueued either way).
+ */
+hn_status hn_kv_archive_evict(const hn_kv_cache* cache, const hn_seg_layout* seg,
+                              hn_kv_archive* archive, hipStream_t stream);
+
+/* Rewind the cache to an earlier segment boundary: the state right after
+ * `segments` segments were appended, when it had seen `frames_seen` latent
+ * frames and held `head_tokens` head tokens (as saved from the counters at
+ * that time).  History frames of that window which the ring has since given
+ * up are copied back from the archive into their ring slots (host-to-device,
+ * on the stream); frames the ring still holds stay; the archive keeps only
+ * the frames older than that window; head tokens past head_tokens are
+ * dropped.  Later appends continue from the rewound state.  Errors:
+ * HN_ERR_INVALID if the target is not earlier than or equal to the current
+ * counters; HN_ERR_CAPACITY if the archive lacks a frame the window needs.
+ */
+hn_status hn_kv_cache_rewind(hn_kv_cache* cache, hn_kv_archive* archive, int64_t frames_seen,
+                             int32_t head_tokens, int32_t segments, hipStream_t stream);
+
 /* Optional block-sparse keep list (device memory, caller-owned).
  *
  * After the first two denoising steps only 25% of the candidate video blocks

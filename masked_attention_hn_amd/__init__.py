@@ -9,9 +9,9 @@ package without it raises ImportError, and there is no fallback path.
 The exported functions carry the C names:
     hn_kv_quant_append, hn_attn_mask_build, hn_seg_attn_fwd,
     hn_attn_workspace_size, hn_kv_cache_sizes, hn_kv_cache_reset,
-    hn_status_string, hn_last_error
-plus small helpers (KVCache, SegLayout, BlockSparse, build_plan,
-dense_mask) that own the buffers those calls need.
+    hn_kv_archive_evict, hn_kv_cache_rewind, hn_status_string, hn_last_error
+plus small helpers (KVCache, KVArchive, SegLayout, BlockSparse, build_plan,
+dense_mask, seg_attn, seg_attn_joint) that own the buffers those calls need.
 """
 from __future__ import annotations
 
@@ -75,6 +75,12 @@ class hn_tile_plan(ctypes.Structure):
                 ("visible_pairs_text", ctypes.c_int64)]
 
 
+class hn_kv_archive(ctypes.Structure):
+    _fields_ = [("k", _vp), ("v", _vp), ("ks", _vp), ("vs", _vp),
+                ("cap_frames", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("first_frame", ctypes.c_int64), ("frames", ctypes.c_int64)]
+
+
 _S = ctypes.c_int
 _lib.hn_status_string.argtypes = [_S]
 _lib.hn_status_string.restype = ctypes.c_char_p
@@ -103,8 +109,16 @@ _lib.hn_seg_attn_fwd.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_
                                  ctypes.c_float, _vp]
 _lib.hn_seg_attn_fwd.restype = _S
 
+_lib.hn_kv_archive_evict.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
+                                     ctypes.POINTER(hn_kv_archive), _vp]
+_lib.hn_kv_archive_evict.restype = _S
+_lib.hn_kv_cache_rewind.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_kv_archive),
+                                    ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
+_lib.hn_kv_cache_rewind.restype = _S
+
 EXPORTS = ["hn_status_string", "hn_last_error", "hn_kv_cache_sizes", "hn_kv_cache_reset",
-           "hn_kv_quant_append", "hn_attn_workspace_size", "hn_attn_mask_build", "hn_seg_attn_fwd"]
+           "hn_kv_quant_append", "hn_attn_workspace_size", "hn_attn_mask_build", "hn_seg_attn_fwd",
+           "hn_kv_archive_evict", "hn_kv_cache_rewind"]
 
 
 class HNError(RuntimeError):
@@ -212,6 +226,41 @@ class KVCache:
     @property
     def segments(self) -> int:
         return self.c.segments
+
+
+class KVArchive:
+    """Pinned host buffers of the history archive (allocated here with torch,
+    pin_memory=True) plus the library's counter struct."""
+
+    def __init__(self, num_heads: int, tokens_per_frame: int, cap_frames: int):
+        H, P, C = num_heads, tokens_per_frame, cap_frames
+        self.k = torch.zeros((H, max(C, 1) * P, HEAD_DIM), dtype=torch.int8, pin_memory=True)
+        self.v = torch.zeros_like(self.k, pin_memory=True)
+        self.ks = torch.zeros((H, max(C, 1) * P), dtype=torch.float32, pin_memory=True)
+        self.vs = torch.zeros_like(self.ks, pin_memory=True)
+        self.c = hn_kv_archive(self.k.data_ptr(), self.v.data_ptr(), self.ks.data_ptr(),
+                               self.vs.data_ptr(), C, 0, 0, 0)
+
+    @property
+    def frames(self) -> int:
+        return self.c.frames
+
+    @property
+    def first_frame(self) -> int:
+        return self.c.first_frame
+
+
+def hn_kv_archive_evict(cache: KVCache, seg: SegLayout, archive: KVArchive, stream=None):
+    _check(_lib.hn_kv_archive_evict(ctypes.byref(cache.c), ctypes.byref(seg.c),
+                                    ctypes.byref(archive.c), _stream(stream)))
+
+
+def hn_kv_cache_rewind(cache: KVCache, archive: Optional[KVArchive], frames_seen: int,
+                       head_tokens: int, segments: int, stream=None):
+    _check(_lib.hn_kv_cache_rewind(ctypes.byref(cache.c),
+                                   ctypes.byref(archive.c) if archive is not None else None,
+                                   int(frames_seen), int(head_tokens), int(segments),
+                                   _stream(stream)))
 
 
 def hn_kv_cache_reset(cache: KVCache):

@@ -182,6 +182,53 @@ hn_status hip_fail(hipError_t e, const char* what) {
   return fail(HN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Global frames [g0, g1) that leave the W-frame window when F frames are
+// appended after fs (see hn_kv_archive_evict in hn.h).
+void evicted_range(int64_t fs, int64_t F, int64_t W, int64_t* g0, int64_t* g1) {
+  const int64_t kept_before = std::min(fs, W);
+  const int64_t kept_after = std::min(fs + F, W);
+  *g0 = fs - kept_before;
+  *g1 = std::max(*g0, std::min(fs, fs + F - kept_after));
+}
+
+hn_status check_archive(const hn_kv_archive* a) {
+  if (!a) return fail(HN_ERR_NULL, "archive is NULL");
+  if (a->cap_frames < 0 || a->frames < 0 || a->frames > a->cap_frames || a->first_frame < 0)
+    return fail(HN_ERR_INVALID, "archive counters are inconsistent");
+  if (a->cap_frames > 0 && (!a->k || !a->v || !a->ks || !a->vs))
+    return fail(HN_ERR_NULL, "archive buffers are NULL");
+  return HN_OK;
+}
+
+// Copy global frames [g0, g1) between their ring slots and the archive (both
+// head-major), in runs that do not wrap the ring: per tensor one 2-D copy of
+// H rows of run*P tokens.
+hn_status archive_copy(const hn_kv_cache* c, const hn_kv_archive* a, int64_t g0, int64_t g1, bool to_host,
+                       hipStream_t stream) {
+  const int64_t W = c->window_frames, P = c->tokens_per_frame, H = c->num_heads;
+  const size_t ring_rows = (size_t)(W * P), arch_rows = (size_t)a->cap_frames * P;
+  const hipMemcpyKind kind = to_host ? hipMemcpyDeviceToHost : hipMemcpyHostToDevice;
+  for (int64_t g = g0; g < g1;) {
+    const int64_t slot = g % W;
+    const int64_t n = std::min(g1 - g, W - slot);
+    const size_t r_row = (size_t)(slot * P), a_row = (size_t)((g - a->first_frame) * P);
+    struct { void* ring; void* arch; size_t elem; } t[4] = {
+        {c->ring_k, a->k, HN_HEAD_DIM}, {c->ring_v, a->v, HN_HEAD_DIM},
+        {c->ring_ks, a->ks, sizeof(float)}, {c->ring_vs, a->vs, sizeof(float)}};
+    for (const auto& x : t) {
+      char* ring = static_cast<char*>(x.ring) + r_row * x.elem;
+      char* arch = static_cast<char*>(x.arch) + a_row * x.elem;
+      const size_t width = (size_t)n * P * x.elem;
+      const size_t rp = ring_rows * x.elem, ap = arch_rows * x.elem;
+      const hipError_t e = to_host ? hipMemcpy2DAsync(arch, ap, ring, rp, width, (size_t)H, kind, stream)
+                                   : hipMemcpy2DAsync(ring, rp, arch, ap, width, (size_t)H, kind, stream);
+      if (e != hipSuccess) return hip_fail(e, to_host ? "archive copy to host" : "archive copy to device");
+    }
+    g += n;
+  }
+  return HN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +308,61 @@ hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void*
   c->frames_seen += s->frames;
   c->head_tokens += s->head_len;
   c->segments += 1;
+  return ok();
+}
+
+hn_status hn_kv_archive_evict(const hn_kv_cache* c, const hn_seg_layout* s, hn_kv_archive* a,
+                              hipStream_t stream) {
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  int64_t tl = 0;
+  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  if ((st = check_archive(a)) != HN_OK) return st;
+  if (s->index != c->segments)
+    return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
+  int64_t g0 = 0, g1 = 0;
+  evicted_range(c->frames_seen, s->frames, c->window_frames, &g0, &g1);
+  if (g1 == g0) return ok();
+  const int64_t first = a->frames == 0 ? g0 : a->first_frame;
+  if (g0 != first + a->frames)
+    return fail(HN_ERR_ORDER, "evicted frames [%lld, %lld) do not continue the archive (next %lld)",
+                (long long)g0, (long long)g1, (long long)(first + a->frames));
+  if (g1 - first > a->cap_frames)
+    return fail(HN_ERR_CAPACITY, "archive holds %d frames; %lld needed", a->cap_frames,
+                (long long)(g1 - first));
+  hn_kv_archive tmp = *a;
+  tmp.first_frame = first;
+  if ((st = archive_copy(c, &tmp, g0, g1, true, stream)) != HN_OK) return st;
+  a->first_frame = first;
+  a->frames = g1 - first;
+  return ok();
+}
+
+hn_status hn_kv_cache_rewind(hn_kv_cache* c, hn_kv_archive* a, int64_t frames_seen, int32_t head_tokens,
+                             int32_t segments, hipStream_t stream) {
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  if (frames_seen < 0 || frames_seen > c->frames_seen || head_tokens < 0 || head_tokens > c->head_tokens ||
+      segments < 0 || segments > c->segments ||
+      (segments == c->segments && (frames_seen != c->frames_seen || head_tokens != c->head_tokens)))
+    return fail(HN_ERR_INVALID, "rewind target (%lld frames, %d head tokens, %d segments) is not an "
+                "earlier state of (%lld, %d, %d)", (long long)frames_seen, head_tokens, segments,
+                (long long)c->frames_seen, c->head_tokens, c->segments);
+  const int64_t W = c->window_frames;
+  const int64_t lo = frames_seen - std::min(frames_seen, W);            // window of the target state
+  const int64_t in_ring = c->frames_seen - std::min(c->frames_seen, W);  // oldest frame the ring holds
+  const int64_t hi = std::min(frames_seen, in_ring);                     // [lo, hi) must come back
+  if (a && (st = check_archive(a)) != HN_OK) return st;
+  if (hi > lo) {
+    if (!a || a->frames == 0 || lo < a->first_frame || hi > a->first_frame + a->frames)
+      return fail(HN_ERR_CAPACITY, "frames [%lld, %lld) are needed but not in the archive",
+                  (long long)lo, (long long)hi);
+    if ((st = archive_copy(c, a, lo, hi, false, stream)) != HN_OK) return st;
+  }
+  if (a) a->frames = std::max<int64_t>(0, std::min<int64_t>(a->frames, lo - a->first_frame));
+  c->frames_seen = frames_seen;
+  c->head_tokens = head_tokens;
+  c->segments = segments;
   return ok();
 }
 

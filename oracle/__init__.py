@@ -49,6 +49,14 @@ Hy-Nomas world model):
   segments keep).  Keep lists concern video query tiles only, so text
   queries attend densely.
 
+* evicted_frames() / archive_of(): the single-GPU configuration keeps at most
+  W history frames on the GPU and archives earlier history to CPU memory
+  (hyphentech explainer, configuration table, history row; fluxbbs teardown,
+  second trick for the 18-frame window).  Appending F frames to a cache that
+  has seen fs frames keeps the last min(fs + F, W) of all frames; the frames
+  that leave the window are the archived ones, oldest first, each stored as
+  the same INT8 codes and scales the cache held.
+
 * attention(): plain softmax attention in fp64 per head over the masked
   full sequence: s = (q . k) * sm_scale, masked scores are -inf,
   p = exp(s - max) / sum, o = sum p v.  Keys and values of earlier segments
@@ -131,6 +139,44 @@ def token_table(w: Workload) -> Dict[str, np.ndarray]:
 
 def _first_frame(w: Workload, s: int) -> int:
     return sum(seg.frames for seg in w.segments[:s])
+
+
+# ----------------------------------------------------------------- archive
+def evicted_frames(frames_seen: int, frames: int, window: int):
+    """Global latent frames [g0, g1) that leave a W-frame window when `frames`
+    new frames are appended after `frames_seen`: the window held
+    [fs - min(fs, W), fs) and holds [fs + F - min(fs + F, W), fs + F) after."""
+    kept_before = min(frames_seen, window)
+    kept_after = min(frames_seen + frames, window)
+    g0 = frames_seen - kept_before
+    g1 = max(g0, min(frames_seen, frames_seen + frames - kept_after))
+    return g0, g1
+
+
+def archive_of(w: Workload, data: dict, upto: int):
+    """INT8 codes and scales of every history frame evicted while segments
+    0 .. upto-1 are appended, in global frame order: (k, v, ks, vs) with
+    shapes [frames][P][H][D] int8 and [frames][P][H] float32."""
+    P = w.segments[0].tokens_per_frame
+    ks, vs, kss, vss = [], [], [], []
+    fs = 0
+    frames_src = []  # (segment, local frame) of every global frame
+    for s in range(upto):
+        seg = w.segments[s]
+        g0, g1 = evicted_frames(fs, seg.frames, w.ring_frames)
+        for g in range(g0, g1):
+            sg, f = frames_src[g]
+            rows = slice(f * P, (f + 1) * P)
+            qk, sk = quantize(data["segments"][sg]["k_vid"][rows])
+            qv, sv = quantize(data["segments"][sg]["v_vid"][rows])
+            ks.append(qk); vs.append(qv); kss.append(sk); vss.append(sv)
+        frames_src += [(s, f) for f in range(seg.frames)]
+        fs += seg.frames
+    if not ks:
+        H, D = w.heads, w.head_dim
+        return (np.zeros((0, P, H, D), np.int8), np.zeros((0, P, H, D), np.int8),
+                np.zeros((0, P, H), np.float32), np.zeros((0, P, H), np.float32))
+    return np.stack(ks), np.stack(vs), np.stack(kss), np.stack(vss)
 
 
 # -------------------------------------------------------------------- mask

@@ -187,3 +187,41 @@ def test_automatic_split_only_for_small_grids(monkeypatch):
     o = -(-(n_vt * 128 * 128 * 4) // 256) * 256
     lse = -(-(n_vt * 128 * 4) // 256) * 256
     assert plan_sizes[1] == spans + o + lse
+
+
+def test_archive_checks():
+    """Validation of hn_kv_archive_evict / hn_kv_cache_rewind on the host
+    (cases that copy nothing; the copies themselves are GPU tests)."""
+    c = fake_cache(H=2, P=24, W=4)
+    s = seg_c()                      # 2 frames
+    ar = hn.hn_kv_archive(FAKE, FAKE, FAKE, FAKE, 8, 0, 0, 0)
+    ev = hn._lib.hn_kv_archive_evict
+    rw = hn._lib.hn_kv_cache_rewind
+    # nothing leaves a window that is not yet full: OK, archive unchanged
+    assert ev(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(ar), None) == hn.HN_OK
+    assert ar.frames == 0
+    assert ev(ctypes.byref(c), ctypes.byref(s.c), None, None) == hn.HN_ERR_NULL
+    bad = hn.hn_kv_archive(FAKE, FAKE, FAKE, FAKE, 8, 0, 0, 9)   # frames > capacity
+    assert ev(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad), None) == hn.HN_ERR_INVALID
+    assert ev(ctypes.byref(c), ctypes.byref(seg_c(index=1).c), ctypes.byref(ar), None) == hn.HN_ERR_ORDER
+    # full window (6 frames seen, W = 4): appending 2 frames evicts frames 2, 3
+    c.frames_seen, c.segments = 6, 0
+    small = hn.hn_kv_archive(FAKE, FAKE, FAKE, FAKE, 1, 0, 0, 0)
+    assert ev(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(small), None) == hn.HN_ERR_CAPACITY
+    gap = hn.hn_kv_archive(FAKE, FAKE, FAKE, FAKE, 8, 0, 0, 1)    # holds frame 0 only: 1 is missing
+    assert ev(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(gap), None) == hn.HN_ERR_ORDER
+    assert small.frames == 0 and gap.frames == 1
+    # rewind: targets must be earlier states
+    c.frames_seen, c.head_tokens, c.segments = 6, 16, 3
+    assert rw(ctypes.byref(c), None, 7, 16, 2, None) == hn.HN_ERR_INVALID
+    assert rw(ctypes.byref(c), None, 6, 20, 2, None) == hn.HN_ERR_INVALID
+    assert rw(ctypes.byref(c), None, 4, 16, 3, None) == hn.HN_ERR_INVALID   # same segments, other frames
+    # the window of frames_seen = 2 is frames [0, 2), no longer in the ring
+    # (it holds [2, 6)) and not archived
+    assert rw(ctypes.byref(c), None, 2, 8, 1, None) == hn.HN_ERR_CAPACITY
+    assert (c.frames_seen, c.head_tokens, c.segments) == (6, 16, 3)
+    # a target whose window the ring still holds needs no archive
+    assert rw(ctypes.byref(c), None, 6, 16, 3, None) == hn.HN_OK
+    c.frames_seen, c.segments = 3, 2      # window [0, 3) with W = 4: all in the ring
+    assert rw(ctypes.byref(c), None, 2, 8, 1, None) == hn.HN_OK
+    assert (c.frames_seen, c.head_tokens, c.segments) == (2, 8, 1)

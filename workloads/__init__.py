@@ -134,6 +134,10 @@ def config(name: str) -> Workload:
         return Workload("c5", 16, [_seg(30, 390, 768, [128] * 4)], 0, None, 1,
                         sparse_keep=0.25, sparse_seed=5)
     # per-GPU share of the 8-way head split at the steady-state shape
+    if name == "arch":
+        # eviction and rewind: 6 segments of 3 latent frames (4x4 tokens), window 4
+        segs = [_seg(3, 16, 8, [4, 4], [(0, 1), (1, 3)]) for _ in range(6)]
+        return Workload("arch", 2, segs, 3, 4, 9)
     if name == "c3_h2":
         s = [_seg(30, 880, 768, [128] * 4) for _ in range(4)]
         return Workload("c3_h2", 2, s, 3, 18, 3)
@@ -160,7 +164,7 @@ def config(name: str) -> Workload:
 
 
 ALL_CONFIGS = ["c1", "c1_evict", "c1_future", "c2", "c3", "c4", "c5", "c3_h2",
-               "m1", "m2", "m3", "m4"]
+               "m1", "m2", "m3", "m4", "arch"]
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
