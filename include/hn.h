@@ -342,6 +342,31 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* cache, const hn_seg_layout* seg,
                           void* o_vid, void* o_txt, float* lse, float* lse_txt,
                           float sm_scale, hipStream_t stream);
 
+/* Camera cross-attention of the current segment's video tokens.
+ *
+ * Each latent frame carries one camera token (four consecutive frame poses
+ * folded into a 64-dimensional vector, linearly projected with a residual
+ * MLP), and in every MMDiT block the video tokens read the time-aligned
+ * camera tokens of their own segment by cross-attention; relative poses are
+ * computed inside the segment ([T] "架构", camera paragraph; [G] "这是什么",
+ * extrinsics cross-attention path).  The projections need trained weights
+ * and are outside this library: the camera tokens' keys and values come in.
+ * The video token at local latent frame f sees camera tokens f' of the same
+ * segment with |f' - f| <= radius:
+ *   O[q] = sum_{f'} softmax(sm_scale * Q[q].K_cam[f']) V_cam[f']
+ * radius 0 is the stated time alignment (one key, weight exactly 1: O is
+ * the frame's camera value); larger radii widen it.
+ *
+ * q_vid        : bf16 [F*P][H][D] (device)
+ * k_cam, v_cam : bf16 [F][H][D] (device), one token per latent frame
+ * o_vid        : bf16 [F*P][H][D] (output; must not alias the inputs)
+ * lse          : fp32 [H][F*P] natural-log softmax normaliser, or NULL
+ * Errors: HN_ERR_NULL, HN_ERR_INVALID (shape, radius < 0, non-finite scale).
+ */
+hn_status hn_camera_attn_fwd(const hn_seg_layout* seg, int32_t num_heads, int32_t radius,
+                             const void* q_vid, const void* k_cam, const void* v_cam,
+                             void* o_vid, float* lse, float sm_scale, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -9,7 +9,8 @@ package without it raises ImportError, and there is no fallback path.
 The exported functions carry the C names:
     hn_kv_quant_append, hn_attn_mask_build, hn_seg_attn_fwd,
     hn_attn_workspace_size, hn_kv_cache_sizes, hn_kv_cache_reset,
-    hn_kv_archive_evict, hn_kv_cache_rewind, hn_status_string, hn_last_error
+    hn_kv_archive_evict, hn_kv_cache_rewind, hn_camera_attn_fwd,
+    hn_status_string, hn_last_error
 plus small helpers (KVCache, KVArchive, SegLayout, BlockSparse, build_plan,
 dense_mask, seg_attn, seg_attn_joint) that own the buffers those calls need.
 """
@@ -116,9 +117,13 @@ _lib.hn_kv_cache_rewind.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(
                                     ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _vp]
 _lib.hn_kv_cache_rewind.restype = _S
 
+_lib.hn_camera_attn_fwd.argtypes = [ctypes.POINTER(hn_seg_layout), ctypes.c_int32, ctypes.c_int32,
+                                    _vp, _vp, _vp, _vp, _vp, ctypes.c_float, _vp]
+_lib.hn_camera_attn_fwd.restype = _S
+
 EXPORTS = ["hn_status_string", "hn_last_error", "hn_kv_cache_sizes", "hn_kv_cache_reset",
            "hn_kv_quant_append", "hn_attn_workspace_size", "hn_attn_mask_build", "hn_seg_attn_fwd",
-           "hn_kv_archive_evict", "hn_kv_cache_rewind"]
+           "hn_kv_archive_evict", "hn_kv_cache_rewind", "hn_camera_attn_fwd"]
 
 
 class HNError(RuntimeError):
@@ -377,3 +382,22 @@ def seg_attn_joint(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, q_txt, k_t
     hn_seg_attn_fwd(cache, seg, plan, q_vid, k_txt, v_txt, k_vid, v_vid, o, lse, sm_scale, stream,
                     q_txt=q_txt, o_txt=o_txt, lse_txt=lse_txt)
     return o, o_txt, lse, lse_txt
+
+
+def hn_camera_attn_fwd(seg: SegLayout, num_heads: int, radius: int, q_vid, k_cam, v_cam,
+                       o_vid: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                       sm_scale: Optional[float] = None, stream=None):
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _check(_lib.hn_camera_attn_fwd(ctypes.byref(seg.c), int(num_heads), int(radius), _ptr(q_vid),
+                                   _ptr(k_cam), _ptr(v_cam), _ptr(o_vid), _ptr(lse), float(sm_scale),
+                                   _stream(stream)))
+
+
+def camera_attn(seg: SegLayout, num_heads: int, q_vid, k_cam, v_cam, radius: int = 0,
+                sm_scale: Optional[float] = None, stream=None):
+    """Allocate the outputs and run hn_camera_attn_fwd; returns (o, lse)."""
+    o = torch.empty_like(q_vid)
+    lse = torch.empty((num_heads, seg.video_len), dtype=torch.float32, device=q_vid.device)
+    hn_camera_attn_fwd(seg, num_heads, radius, q_vid, k_cam, v_cam, o, lse, sm_scale, stream)
+    return o, lse

@@ -1,0 +1,101 @@
+// Camera cross-attention of a segment's video tokens (gfx950).
+//
+// Each latent frame carries one camera token (four frame poses folded into a
+// 64-dimensional vector and projected), and in every block the video tokens
+// read the time-aligned camera tokens of their own segment by cross-attention
+// ("Hy-Nomas 拆解" teardown, section "架构", camera paragraph).  The video
+// token at latent frame f sees the camera tokens of frames f' with
+// |f' - f| <= radius; radius 0 is the time alignment the pages state (one
+// key, weight exactly 1, so O is that frame's camera value).
+//
+// HBM-bound: per (token, head) it reads the 256-byte query and writes the
+// 256-byte output (+ 4 bytes of lse); the camera keys and values (F x H x 256
+// bytes each) stay in cache.  8 lanes own one row (16 values each, 32-byte
+// loads and stores); the score is an 8-lane butterfly; online softmax over
+// the visible camera tokens in fp32.
+#include "hn_internal.h"
+
+namespace hn {
+namespace {
+
+constexpr int LANES = 8;            // lanes per (token, head) row
+constexpr int ROWS = 256 / LANES;   // rows per block
+
+__device__ inline void load16(const __bf16* p, float (&x)[16]) {
+  const uint4 a = *reinterpret_cast<const uint4*>(p);
+  const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+__device__ inline float sum8(float x) {
+  x += __shfl_xor(x, 1);
+  x += __shfl_xor(x, 2);
+  x += __shfl_xor(x, 4);
+  return x;
+}
+
+__global__ __launch_bounds__(256) void camera_attn_kernel(CameraParams p) {
+  const int lane = threadIdx.x & (LANES - 1);
+  const int64_t unit = (int64_t)blockIdx.x * ROWS + (threadIdx.x / LANES);
+  // whole 8-lane groups leave together, so the butterflies stay inside active lanes
+  if (unit >= p.rows * p.H) return;
+  const int64_t t = unit / p.H;
+  const int h = (int)(unit - t * p.H);
+  const int f = (int)(t / p.P);
+  const int lo = max(0, f - p.radius);
+  const int hi = min(p.F, f + p.radius + 1);
+
+  float q[16];
+  load16(p.q + (t * p.H + h) * D + lane * 16, q);
+  float m = -INFINITY, l = 0.0f;
+  float acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int g = lo; g < hi; ++g) {
+    const int64_t kv = ((int64_t)g * p.H + h) * D + lane * 16;
+    float k[16];
+    load16(p.k + kv, k);
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(q[i], k[i], s);
+    s = sum8(s) * p.scale_log2;
+    const float m_new = fmaxf(m, s);
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float w = __builtin_amdgcn_exp2f(s - m_new);
+    float v[16];
+    load16(p.v + kv, v);
+    l = l * alpha + w;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = acc[i] * alpha + w * v[i];
+    m = m_new;
+  }
+  const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bf16x2_t pr = {(__bf16)(acc[2 * i] * inv), (__bf16)(acc[2 * i + 1] * inv)};
+    o[i] = __builtin_bit_cast(uint32_t, pr);
+  }
+  __bf16* dst = p.o + (t * p.H + h) * D + lane * 16;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
+  *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  if (p.lse != nullptr && lane == 0)
+    p.lse[(int64_t)h * p.rows + t] = l > 0.0f ? (m + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
+}
+
+}  // namespace
+
+hipError_t launch_camera_attn(const CameraParams& p, hipStream_t s) {
+  const int64_t units = p.rows * p.H;
+  if (units == 0) return hipSuccess;
+  const int64_t blocks = (units + ROWS - 1) / ROWS;
+  hipLaunchKernelGGL(camera_attn_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace hn

@@ -537,4 +537,35 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   return ok();
 }
 
+hn_status hn_camera_attn_fwd(const hn_seg_layout* s, int32_t num_heads, int32_t radius, const void* q_vid,
+                             const void* k_cam, const void* v_cam, void* o_vid, float* lse, float sm_scale,
+                             hipStream_t stream) {
+  if (!s) return fail(HN_ERR_NULL, "segment layout is NULL");
+  if (s->frames < 1 || s->tokens_per_frame < 1)
+    return fail(HN_ERR_INVALID, "segment of %d frames x %d tokens", s->frames, s->tokens_per_frame);
+  if (num_heads < 1) return fail(HN_ERR_INVALID, "num_heads %d < 1", num_heads);
+  if (radius < 0) return fail(HN_ERR_INVALID, "radius %d < 0", radius);
+  if (!q_vid || !k_cam || !v_cam || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o pointer is NULL");
+  if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
+  const int64_t rows = (int64_t)s->frames * s->tokens_per_frame;
+  if (rows * num_heads > ((int64_t)1 << 40))
+    return fail(HN_ERR_UNSUPPORTED, "segment of %lld tokens x %d heads too large", (long long)rows, num_heads);
+  hn::CameraParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.H = num_heads;
+  p.P = s->tokens_per_frame;
+  p.F = s->frames;
+  p.radius = std::min(radius, s->frames);
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.rows = rows;
+  p.q = static_cast<const __bf16*>(q_vid);
+  p.k = static_cast<const __bf16*>(k_cam);
+  p.v = static_cast<const __bf16*>(v_cam);
+  p.o = static_cast<__bf16*>(o_vid);
+  p.lse = lse;
+  hipError_t e = hn::launch_camera_attn(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "camera attention launch");
+  return ok();
+}
+
 }  // extern "C"

@@ -173,6 +173,24 @@ struct DenseParams {
   uint8_t* out;
 };
 
+// Camera cross-attention of the video tokens of one segment.
+struct CameraParams {
+  int32_t H;
+  int32_t P;             // tokens per latent frame
+  int32_t F;             // latent frames (= camera tokens)
+  int32_t radius;        // visible camera tokens: |f' - f| <= radius
+  float scale_log2;      // sm_scale * log2(e)
+  int32_t pad0;
+  int64_t rows;          // F * P video tokens
+  const __bf16* q;       // [rows][H][D]
+  const __bf16* k;       // [F][H][D]
+  const __bf16* v;       // [F][H][D]
+  __bf16* o;             // [rows][H][D]
+  float* lse;            // [H][rows] or null
+};
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 // Query rows per tile of a dense (keep-list free) plan; keep-list plans use HN_TILE.
 int attn_dense_rows();
 
@@ -182,5 +200,6 @@ hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s);
 hipError_t launch_dense(const DenseParams& p, hipStream_t s);
 hipError_t launch_attn(const AttnParams& p, hipStream_t s);
 hipError_t launch_merge(const MergeParams& p, hipStream_t s);
+hipError_t launch_camera_attn(const CameraParams& p, hipStream_t s);
 
 }  // namespace hn

@@ -57,6 +57,17 @@ Hy-Nomas world model):
   that leave the window are the archived ones, oldest first, each stored as
   the same INT8 codes and scales the cache held.
 
+* camera_attention(): each latent frame has one camera token (four frame
+  poses folded into a 64-dimensional vector and projected), and in every
+  block the video tokens read, by cross-attention, the time-aligned camera
+  tokens of their own segment (fluxbbs teardown, "Architecture", camera
+  paragraph; papers.ananclaw guide, "What it is": the extrinsics
+  cross-attention path).  The projections need trained weights, so the
+  camera tokens' keys and values are inputs.  Reading of "time-aligned": a
+  video token at latent frame f sees the camera tokens of frames f' of its
+  segment with |f' - f| <= radius; radius 0 (its own frame's token only) is
+  the pages' statement, larger radii a generalization.
+
 * attention(): plain softmax attention in fp64 per head over the masked
   full sequence: s = (q . k) * sm_scale, masked scores are -inf,
   p = exp(s - max) / sum, o = sum p v.  Keys and values of earlier segments
@@ -346,6 +357,33 @@ def attention(w: Workload, data: dict, rows: Optional[Sequence[int]] = None,
             lse[h, c0:c0 + len(r)] = m[:, 0] + np.log(l[:, 0])
             rsum[h, c0:c0 + len(r)] = np.sum(p, axis=1)
     return O, lse, rsum
+
+
+def camera_attention(w: Workload, data: dict, radius: int = 0,
+                     sm_scale: Optional[float] = None):
+    """Cross-attention of the query segment's video tokens to its camera
+    tokens in fp64: query row r (latent frame f = r // P) sees camera tokens
+    f' with |f' - f| <= radius.  Returns (O [rows][H][D], lse [H][rows])."""
+    cur = w.current
+    H, D, P, F = w.heads, w.head_dim, cur.tokens_per_frame, cur.frames
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    Q = bf16_bits_to_f32(data["q_vid"]).astype(np.float64)
+    K = bf16_bits_to_f32(data["k_cam"]).astype(np.float64)
+    V = bf16_bits_to_f32(data["v_cam"]).astype(np.float64)
+    O = np.zeros((cur.video_len, H, D))
+    lse = np.zeros((H, cur.video_len))
+    for f in range(F):
+        lo, hi = max(0, f - radius), min(F, f + radius + 1)
+        rows = slice(f * P, (f + 1) * P)
+        for h in range(H):
+            s = (Q[rows, h, :] @ K[lo:hi, h, :].T) * sm_scale
+            m = np.max(s, axis=1, keepdims=True)
+            e = np.exp(s - m)
+            l = np.sum(e, axis=1, keepdims=True)
+            O[rows, h, :] = (e / l) @ V[lo:hi, h, :]
+            lse[h, rows] = m[:, 0] + np.log(l[:, 0])
+    return O, lse
 
 
 def effective_flops_text(w: Workload) -> float:

@@ -225,3 +225,14 @@ def test_archive_checks():
     c.frames_seen, c.segments = 3, 2      # window [0, 3) with W = 4: all in the ring
     assert rw(ctypes.byref(c), None, 2, 8, 1, None) == hn.HN_OK
     assert (c.frames_seen, c.head_tokens, c.segments) == (2, 8, 1)
+
+
+def test_camera_checks():
+    s = seg_c()
+    cam = hn._lib.hn_camera_attn_fwd
+    args = [FAKE, FAKE, FAKE, FAKE, None]   # q, k_cam, v_cam, o, lse
+    assert cam(None, 2, 0, *args, 0.1, None) == hn.HN_ERR_NULL
+    assert cam(ctypes.byref(s.c), 0, 0, *args, 0.1, None) == hn.HN_ERR_INVALID
+    assert cam(ctypes.byref(s.c), 2, -1, *args, 0.1, None) == hn.HN_ERR_INVALID
+    assert cam(ctypes.byref(s.c), 2, 0, *args, float("inf"), None) == hn.HN_ERR_INVALID
+    assert cam(ctypes.byref(s.c), 2, 0, FAKE, None, FAKE, FAKE, None, 0.1, None) == hn.HN_ERR_NULL

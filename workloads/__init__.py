@@ -194,8 +194,10 @@ def generate(w: Workload) -> Dict[str, object]:
 
     Draw order: for every segment in sequence order, K_txt, V_txt, K_vid,
     V_vid (each [tokens][H][D]); then Q_vid of the query segment, then its
-    Q_txt (text-stream queries: head and tail tokens).  Queries are always
-    N(0,1); keys and values follow w.kv_dist.
+    Q_txt (text-stream queries: head and tail tokens), then the keys and
+    values of its camera tokens K_cam, V_cam ([frames][H][D], one token per
+    latent frame).  Queries and camera tokens are always N(0,1); keys and
+    values follow w.kv_dist.
     """
     rng = np.random.default_rng(w.seed)
     H, D = w.heads, w.head_dim
@@ -209,7 +211,9 @@ def generate(w: Workload) -> Dict[str, object]:
         })
     q = _draw(rng, (w.current.video_len, H, D), "normal")
     qt = _draw(rng, (w.current.text_len, H, D), "normal")
-    out = {"segments": segs, "q_vid": q, "q_txt": qt}
+    kc = _draw(rng, (w.current.frames, H, D), "normal")
+    vc = _draw(rng, (w.current.frames, H, D), "normal")
+    out = {"segments": segs, "q_vid": q, "q_txt": qt, "k_cam": kc, "v_cam": vc}
     if w.sparse_keep is not None:
         out["csr"] = block_sparse_csr(w)
     return out
