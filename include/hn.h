@@ -250,7 +250,8 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
  * writes a partial result into the workspace and a merge kernel combines
  * them (one softmax, exactly as without the split up to rounding).  The
  * split count comes from the device's compute-unit count and the layout;
- * HN_ATTN_SPLITS=n in the environment forces n (1..16).  With n_splits > 1
+ * HN_ATTN_SPLITS=n in the environment forces n (1..16).  Dense plans use
+ * 256-row query tiles (HN_ATTN_DENSE_ROWS=128 forces 128-row ones).  With n_splits > 1
  * attention calls that share one plan workspace must not overlap in time
  * (same stream, or ordered), since they write its partial area. */
 typedef struct hn_tile_plan {

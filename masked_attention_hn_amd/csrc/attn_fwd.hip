@@ -619,19 +619,21 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   }
 }
 
-// Dense and keep-list plans both use 128-row blocks of 4 waves x 32 rows with
-// two blocks per CU (two waves per SIMD from independent blocks, which drift
-// out of phase so one block's MFMAs overlap the other's softmax).  Measured
-// alternatives: 8-wave 256-row blocks (c3/c4 slower), 4 waves x 64 rows at
-// one wave per SIMD (much slower), 128-key tiles (spill).
+// Dense plans use 256-row blocks of 8 waves x 32 rows, one block per CU (two
+// waves per SIMD): every staged (and, for INT8, dequantized) key/value tile
+// serves 256 query rows.  Measured against 128-row 4-wave blocks at two per
+// CU: +3% on the 480x832 segment, +2% on the 1280x704 steady state, +13% on
+// the 7th 1280x704 segment with 158k INT8 history keys.  Keep-list plans use
+// 128-row blocks (the keep list's query tile).  Also measured: 4 waves x 64
+// rows at one wave per SIMD (much slower), 128-key tiles (spill).
 #ifndef HN_DENSE_NW
-#define HN_DENSE_NW 4
+#define HN_DENSE_NW 8
 #endif
 #ifndef HN_DENSE_QB
 #define HN_DENSE_QB 1
 #endif
 #ifndef HN_DENSE_MINB
-#define HN_DENSE_MINB 2
+#define HN_DENSE_MINB 1
 #endif
 using DenseCfg = Cfg<HN_DENSE_NW, HN_DENSE_QB, 64>;
 using SparseCfg = Cfg<4, 1, 64>;

@@ -92,14 +92,14 @@ int device_cus() {
 }
 
 // Key splits per query tile (split-KV).  Measured on MI355X, splitting does
-// not pay once the grid has at least one block per compute unit: a CU
-// holding one 4-wave block runs it nearly as fast as it runs two, and the
-// fp32 partial results plus the merge cost more than the better fill (the
-// 2-head share of the 1280x704 steady state, 414 blocks on 256 CUs: 1.54 ms
-// unsplit, 1.73 / 1.59 / 1.61 / 1.56 ms with 2 / 3 / 4 / 8 splits).  So only
-// grids with fewer blocks than CUs are split, to about two blocks per CU and
-// no fewer than 1024 keys per split.  HN_ATTN_SPLITS=n in the environment
-// forces n (tuning and tests).
+// not pay while the grid covers even half the compute units: the fp32
+// partial results plus the merge cost more than the better fill.  The 2-head
+// share of the 1280x704 steady state (208 blocks of 256 rows on 256 CUs)
+// takes 1.386 ms unsplit and 1.543 / 1.532 ms with 2 / 3 splits; with
+// 128-row blocks (414 blocks) 1.54 / 1.73 / 1.59 / 1.61 / 1.56 ms with
+// 1 / 2 / 3 / 4 / 8 splits.  So only a grid with at most one block per two
+// CUs is split, to about one block per CU, with no fewer than 1024 keys per
+// split.  HN_ATTN_SPLITS=n in the environment forces n (tuning and tests).
 int choose_splits(int H, int n_qtiles, int64_t keys_per_tile) {
   if (const char* e = std::getenv("HN_ATTN_SPLITS")) {
     const int v = std::atoi(e);
@@ -107,11 +107,26 @@ int choose_splits(int H, int n_qtiles, int64_t keys_per_tile) {
   }
   const int64_t cus = device_cus();
   const int64_t tasks = (int64_t)H * n_qtiles;
-  if (tasks <= 0 || tasks >= cus) return 1;
-  int64_t sp = ceil_div(2 * cus, tasks);
+  if (tasks <= 0 || 2 * tasks > cus) return 1;
+  int64_t sp = ceil_div(cus, tasks);
   sp = std::min<int64_t>(sp, keys_per_tile / 1024);
   sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
   return (int)std::max<int64_t>(sp, 1);
+}
+
+// Query rows per tile of a plan: keep lists fix HN_TILE; dense plans use the
+// kernel's 256-row blocks (faster than 128-row ones even where 256-row blocks
+// leave compute units idle: the 2-head share above runs 1.386 ms with 208
+// such blocks, 1.545 ms with 414 128-row blocks).
+// HN_ATTN_DENSE_ROWS=128|256 in the environment forces the height (tuning, tests).
+int plan_tile_rows(bool sparse) {
+  if (sparse) return HN_TILE;
+  const int rows = hn::attn_dense_rows();
+  if (const char* e = std::getenv("HN_ATTN_DENSE_ROWS")) {
+    const int v = std::atoi(e);
+    if (v == HN_TILE || v == rows) return v;
+  }
+  return rows;
 }
 
 // Plan parameters for the current state; validates the keep list.
@@ -124,7 +139,7 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   std::memset(pp, 0, sizeof(*pp));
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  pp->tile_q = sp ? HN_TILE : hn::attn_dense_rows();
+  pp->tile_q = plan_tile_rows(sp != nullptr);
   pp->n_qtiles = (int)ceil_div(lq, pp->tile_q);
   pp->n_text_tiles = (int)ceil_div(tl, pp->tile_q);
   pp->lq = lq;
@@ -456,7 +471,7 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
     return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  const int want_tile = plan->sparse ? HN_TILE : hn::attn_dense_rows();
+  const int want_tile = plan_tile_rows(plan->sparse != 0);
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
       plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
       plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile) ||

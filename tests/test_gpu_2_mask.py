@@ -23,10 +23,15 @@ def data_of(name):
     return _DATA[name]
 
 
-@pytest.mark.parametrize("name", ["c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4",
-                                  "c2", "c3", "c5"])
-def test_dense_mask_matches_oracle(name):
-    print(f"[mask] {name}", flush=True)
+@pytest.mark.parametrize("name,rows_env", [(n, "auto") for n in
+                                           ("c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4",
+                                            "c2", "c3", "c5")] +
+                         [(n, "128") for n in ("c1", "m1", "m2", "m4", "c2")])
+def test_dense_mask_matches_oracle(name, rows_env, monkeypatch):
+    # the spans are built per plan tile; both tile heights must expand to the oracle mask
+    print(f"[mask] {name} rows={rows_env}", flush=True)
+    if rows_env != "auto":
+        monkeypatch.setenv("HN_ATTN_DENSE_ROWS", rows_env)
     w = W.config(name)
     d = data_of(name)
     run = G.Run(w, d)
