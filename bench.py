@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--workload", default="c2", help="c2 (default), c3, c4 or c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=11700, help="query rows the oracle computes")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the joint, camera and archive measurements (counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -258,10 +260,11 @@ def main():
     # camera cross-attention (radius 0: each video token reads its own latent
     # frame's camera token); rotating query/output sets over 600 MB so the
     # bytes come from HBM
+    camera = None
     k_cam, v_cam = to_dev(data["k_cam"]), to_dev(data["v_cam"])
     cam_rows = w.current.video_len * w.heads
     cam_bytes = cam_rows * (128 * 2 * 2 + 4)
-    n_cam = max(3, math.ceil(600e6 / cam_bytes))
+    n_cam = 0 if args.no_extras else max(3, math.ceil(600e6 / cam_bytes))
     cam_sets = [(q.clone(), torch.empty_like(q),
                  torch.empty((w.heads, w.current.video_len), dtype=torch.float32, device=dev))
                 for _ in range(n_cam)]
@@ -277,8 +280,8 @@ def main():
         hn.hn_camera_attn_fwd(seg, w.heads, 0, qq, k_cam, v_cam, oo, ll)
         ec1[i].record(stream)
     torch.cuda.synchronize()
-    cam_ms = sorted(a.elapsed_time(b) for a, b in zip(ec0, ec1))[reps // 2]
-    camera = {
+    cam_ms = sorted(a.elapsed_time(b) for a, b in zip(ec0, ec1))[reps // 2] if reps else 0.0
+    camera = None if not reps else {
         "kernel": "camera_attn_kernel",
         "what": "video tokens x heads reading their frame's camera token (radius 0)",
         "bound": "hbm",
@@ -295,7 +298,7 @@ def main():
     # this segment pushes out of the window, append, then rewind (host ->
     # device) to the state before it; repeated, each copy timed on the stream
     archive = None
-    if w.window is not None and saved[0] >= w.window:
+    if w.window is not None and saved[0] >= w.window and not args.no_extras:
         P = w.current.tokens_per_frame
         ar = hn.KVArchive(w.heads, P, saved[0] + w.current.frames)
         n_ar = 6
@@ -330,7 +333,7 @@ def main():
 
     # the same call with the segment's text queries added (one launch for both)
     joint = None
-    if w.current.text_len > 0:
+    if w.current.text_len > 0 and not args.no_extras:
         cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
         hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c)
         q_txt = to_dev(data["q_txt"])
