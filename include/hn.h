@@ -334,7 +334,7 @@ hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
  *                iff q_txt is given and h + sum(a) > 0
  * lse, lse_txt : fp32 [H][F*P] / [H][h + sum(a)] natural-log softmax
  *                normalisers, or NULL
- * sm_scale     : score scale, normally 1/sqrt(128)
+ * sm_scale     : score scale > 0, normally 1/sqrt(128) (else HN_ERR_INVALID)
  */
 hn_status hn_seg_attn_fwd(const hn_kv_cache* cache, const hn_seg_layout* seg,
                           const hn_tile_plan* plan, const void* q_vid, const void* q_txt,

@@ -481,7 +481,9 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
   const bool text_q = q_txt != nullptr && tl > 0;
   if (text_q && !o_txt) return fail(HN_ERR_NULL, "o_txt is NULL while q_txt is given");
-  if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
+  // the kernel takes a tile's max over raw scores, valid for a positive scale
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(HN_ERR_INVALID, "sm_scale %g is not a positive finite number", (double)sm_scale);
   // the kernel addresses every source through 32-bit buffer offsets
   const int64_t tok_bytes = (int64_t)c->num_heads * HN_HEAD_DIM * 2;
   const int64_t lim = INT_MAX;

@@ -142,6 +142,8 @@ def test_attention_rejects_stale_plan():
     plan.n_splits = 1
     assert call(s, None) == hn.HN_ERR_NULL
     assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID
+    assert call(s, ctypes.byref(plan), scale=-0.1) == hn.HN_ERR_INVALID   # positive scales only
+    assert call(s, ctypes.byref(plan), scale=0.0) == hn.HN_ERR_INVALID
     # text queries without their output
     assert call(s, ctypes.byref(plan), qq=[FAKE, FAKE]) == hn.HN_ERR_NULL
     s2 = seg_c(index=1)
