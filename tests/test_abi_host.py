@@ -249,3 +249,23 @@ def test_camera_checks():
     assert cam(ctypes.byref(s.c), 2, -1, *args, 0.1, None) == hn.HN_ERR_INVALID
     assert cam(ctypes.byref(s.c), 2, 0, *args, float("inf"), None) == hn.HN_ERR_INVALID
     assert cam(ctypes.byref(s.c), 2, 0, FAKE, None, FAKE, FAKE, None, 0.1, None) == hn.HN_ERR_NULL
+
+
+def test_attention_rejects_sources_over_2gib():
+    """Every key/value source is addressed with 32-bit buffer offsets: a video
+    source of more than 2 GiB (here 600 frames x 880 tokens x 16 heads x 256 B)
+    is refused before anything is enqueued."""
+    c = fake_cache(H=16, P=880, W=18, cap=0)
+    F, P = 600, 880
+    s = hn.SegLayout(0, F, P, 0, [], [], [])
+    fwd = hn._lib.hn_seg_attn_fwd
+    for rows in (128, 256):
+        plan = hn.hn_tile_plan(dev=FAKE, tile_q=rows, n_qtiles=-(-F * P // rows), n_text_tiles=0,
+                               max_spans=4, n_splits=1, visible_pairs=-1)
+        st = fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), FAKE, None, None, None,
+                 FAKE, FAKE, FAKE, None, None, None, 0.1, None)
+        if st != hn.HN_ERR_ORDER:          # the plan height the library uses
+            assert st == hn.HN_ERR_UNSUPPORTED
+            break
+    else:
+        raise AssertionError("no plan height accepted")
