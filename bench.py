@@ -401,6 +401,13 @@ def main():
             "traffic": traffic,
             "avg_launch_ms": round(attn_avg, 4),
         },
+        "memory": {
+            "cache_bytes": sum(t.numel() * t.element_size() for t in (
+                cache.ring_k, cache.ring_v, cache.ring_ks, cache.ring_vs,
+                cache.heads_k, cache.heads_v, cache.heads_ks, cache.heads_vs)),
+            "plan_workspace_bytes": ws.numel(),
+            "peak_allocated_bytes": torch.cuda.max_memory_allocated(),
+        },
         "joint": joint,
         "archive": archive,
         "camera": camera,

@@ -220,6 +220,25 @@ class KVCache:
                              self.heads_k.data_ptr(), self.heads_v.data_ptr(),
                              self.heads_ks.data_ptr(), self.heads_vs.data_ptr(), 0, 0, 0)
 
+    def state_dict(self) -> dict:
+        """Checkpoint of the cache: its buffers copied to host memory plus the
+        counters (the cache is caller-owned buffers and a plain struct)."""
+        names = ("ring_k", "ring_v", "ring_ks", "ring_vs", "heads_k", "heads_v", "heads_ks", "heads_vs")
+        out = {n: getattr(self, n).cpu() for n in names}
+        out["counters"] = (self.c.frames_seen, self.c.head_tokens, self.c.segments)
+        return out
+
+    def load_state_dict(self, state: dict):
+        """Restore a checkpoint taken from a cache of the same shape."""
+        for n, t in state.items():
+            if n == "counters":
+                continue
+            dst = getattr(self, n)
+            if dst.shape != t.shape or dst.dtype != t.dtype:
+                raise ValueError(f"checkpoint {n} has shape {tuple(t.shape)}, cache {tuple(dst.shape)}")
+            dst.copy_(t)
+        self.c.frames_seen, self.c.head_tokens, self.c.segments = state["counters"]
+
     @property
     def frames_seen(self) -> int:
         return self.c.frames_seen
