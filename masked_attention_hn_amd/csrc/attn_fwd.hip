@@ -64,8 +64,10 @@ struct Cfg {
   static constexpr int KBLK = KB * 8;          // 1 KB K-operand blocks per tile
   static constexpr int VBLK = 4 * KB * 2;      // 1 KB V-operand block pairs per tile
   static constexpr int CH8 = 8 * KT / T;       // INT8 16-byte chunks per thread (K and V each)
-  static_assert(KT == 64, "tile shape");
-  static_assert(KBLK % NW == 0 && VBLK % NW == 0 && CH8 >= 1, "load split");
+  static constexpr int RG = KT / 64;           // INT8 staging: 64-row groups; wave w takes rows
+                                               // 64 (w % RG) + lane, chunks of 16 codes w / RG + c NW/RG
+  static_assert(KT == 64 || KT == 128, "tile shape");
+  static_assert(KBLK % NW == 0 && VBLK % NW == 0 && CH8 >= 1 && NW % RG == 0, "load split");
   static_assert(2 * KT <= T, "one scale per thread");
 };
 
@@ -210,18 +212,19 @@ __device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb,
 template <class C>
 __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rks, rsrc_t rvs, int kb,
                                int nk, Prefetch<C>& pf) {
-  static_assert(C::KT == 64, "row = lane");
   // wave index made scalar so that offsets and descriptors stay in SGPRs
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t base = (uint32_t)kb * D;
+  const int rg = wave % C::RG;                         // row group of this wave
+  const uint32_t base = (uint32_t)(kb + 64 * rg) * D;
 #pragma unroll
   for (int c = 0; c < C::CH8; ++c) {
-    const uint32_t dch = c * (C::T / 64) + wave;  // 16-code chunk of row lane%64
+    const uint32_t dch = c * (C::NW / C::RG) + wave / C::RG;  // 16-code chunk of row 64 rg + lane
     pf.k[c] = ld_b128(rk, S.vo_i, base + dch * 16);
     pf.v[c] = ld_b128(rv, S.vo_i, base + dch * 16);
   }
-  // every thread dequantizes row lane%64, so every thread needs its scales
-  const bool ok = (int)(threadIdx.x & 63) < nk;
+  // every thread dequantizes its row, so every thread needs its scales
+  // (vo_sc = (tid % KT) * 4 addresses row 64 rg + lane)
+  const bool ok = (int)(threadIdx.x & 63) + 64 * rg < nk;
   const float ks = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rks, S.vo_sc, (uint32_t)kb * 4, 0));
   const float vs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rvs, S.vo_sc, (uint32_t)kb * 4, 0));
   pf.ks = ks;  // used only after the current tile's math: no wait here
@@ -229,12 +232,13 @@ __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rk
   pf.ok = ok;
 }
 
-// INT8 tile: convert and write the operand-major layouts (row r = tid % 64,
+// INT8 tile: convert and write the operand-major layouts (row r = 64 rg + lane,
 // codes [16 dch, 16 dch + 16)).
 template <class C>
 __device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
   const int tid = threadIdx.x;
-  const int r = tid & 63;
+  const int wave = tid >> 6;
+  const int r = (tid & 63) + 64 * (wave % C::RG);
   const int kb32 = r >> 5, q32 = r & 31;
   // V slot coordinates of row r
   const int h = (r >> 4) & 1, half = (r >> 3) & 1, g = (r >> 2) & 1, qq = r & 3;
@@ -242,7 +246,7 @@ __device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
   const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
 #pragma unroll
   for (int c8 = 0; c8 < C::CH8; ++c8) {
-    const int dch = (c8 * C::T + tid) >> 6;
+    const int dch = c8 * (C::NW / C::RG) + wave / C::RG;
     uint4 lo, hi;
     i8x16_dequant(pf.k[c8], ks, lo, hi);
     // d chunks 2dch (g=0) and 2dch+1 (g=1) of K block (kb32, t = dch)
@@ -635,7 +639,10 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #ifndef HN_DENSE_MINB
 #define HN_DENSE_MINB 1
 #endif
-using DenseCfg = Cfg<HN_DENSE_NW, HN_DENSE_QB, 64>;
+#ifndef HN_DENSE_KT
+#define HN_DENSE_KT 64
+#endif
+using DenseCfg = Cfg<HN_DENSE_NW, HN_DENSE_QB, HN_DENSE_KT>;
 using SparseCfg = Cfg<4, 1, 64>;
 static_assert(SparseCfg::ROWS == HN_TILE, "keep-list blocks must match the keep-list tile");
 
