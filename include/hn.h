@@ -250,7 +250,10 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
  * writes a partial result into the workspace and a merge kernel combines
  * them (one softmax, exactly as without the split up to rounding).  The
  * split count comes from the device's compute-unit count and the layout;
- * HN_ATTN_SPLITS=n in the environment forces n (1..16).  Dense plans use
+ * HN_ATTN_SPLITS=n in the environment forces n (1..16).  Text query tiles,
+ * which follow all video tiles in a joint launch, are split 4 ways when they
+ * visit at least 4096 keys, so that they fill the launch's last round of
+ * blocks (HN_ATTN_TEXT_SPLITS=n forces n).  Dense plans use
  * 256-row query tiles (HN_ATTN_DENSE_ROWS=128 forces 128-row ones).  With n_splits > 1
  * attention calls that share one plan workspace must not overlap in time
  * (same stream, or ordered), since they write its partial area. */
@@ -264,9 +267,11 @@ typedef struct hn_tile_plan {
   int32_t head_tokens;
   int64_t frames_seen;
   int32_t sparse;             /* 1 if a keep list was merged */
-  int32_t n_splits;           /* key splits per query tile (split-KV), 1 .. 16 */
+  int32_t n_splits;           /* key splits per video query tile (split-KV), 1 .. 16 */
   int64_t visible_pairs;      /* unmasked (video query, key) pairs per head; -1 if sparse */
   int64_t visible_pairs_text; /* unmasked (text query, key) pairs per head */
+  int32_t n_splits_text;      /* key splits per text query tile, 1 .. 16 */
+  int32_t reserved0;
 } hn_tile_plan;
 
 /* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments): the span

@@ -73,7 +73,8 @@ class hn_tile_plan(ctypes.Structure):
                 ("seg_index", ctypes.c_int32), ("head_tokens", ctypes.c_int32),
                 ("frames_seen", ctypes.c_int64), ("sparse", ctypes.c_int32),
                 ("n_splits", ctypes.c_int32), ("visible_pairs", ctypes.c_int64),
-                ("visible_pairs_text", ctypes.c_int64)]
+                ("visible_pairs_text", ctypes.c_int64), ("n_splits_text", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
 
 
 class hn_kv_archive(ctypes.Structure):

@@ -427,7 +427,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   if (task >= p.n_tasks) return;  // whole block leaves before any barrier
   const int h = task / p.n_tiles;
   const int vt = task - h * p.n_tiles;  // virtual tile: (query tile, key split), split fastest
-  const int tile = vt / p.n_splits;
+  int tile, split_unused, n_split;
+  vt_decode(vt, p.n_qtiles, p.n_splits, p.n_splits_text, tile, split_unused, n_split);
   // plan tiles: video query tiles, then text query tiles (own head and tails)
   const bool text = tile >= p.n_qtiles;
   const int qt = text ? tile - p.n_qtiles : tile;  // tile within its query set
@@ -548,8 +549,8 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
     const float lse_v = l_tot > 0.0f ? (st[q].m + __log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     if (row[q] >= lq) continue;
-    if (p.n_splits > 1) {
-      const int64_t prow = ((int64_t)h * p.n_vt + vt) * C::ROWS + (row[q] - qt * C::ROWS);
+    if (n_split > 1) {
+      const int64_t prow = ((int64_t)h * p.n_pvt + (vt - p.part_vt0)) * C::ROWS + (row[q] - qt * C::ROWS);
       float* orow = p.part_o + prow * D;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -580,7 +581,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   }
 }
 
-// Split-KV merge: for every (head, query tile) the n_splits partial results
+// Split-KV merge: for every (head, query tile) that was split, the partial results
 // (normalized O in fp32, lse) of the same rows are combined exactly as one
 // softmax over the union of their keys: with M = max_s lse_s and
 // w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
@@ -591,6 +592,8 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int h = blockIdx.x / p.n_tiles;
   const int t = blockIdx.x - h * p.n_tiles;
   const bool text = t >= p.n_qtiles;
+  const int n_split = text ? p.n_splits_text : p.n_splits;
+  if (n_split == 1) return;  // this tile wrote its outputs directly
   const int qt = text ? t - p.n_qtiles : t;
   const int lq = text ? p.lq_txt : p.lq;
   __bf16* out = text ? p.o_txt : p.o;
@@ -599,13 +602,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   for (int rl = threadIdx.x >> 5; rl < p.tile_rows; rl += 8) {
     const int row = qt * p.tile_rows + rl;
     if (row >= lq) break;
-    const int64_t base = ((int64_t)h * p.n_vt + (int64_t)t * p.n_splits) * p.tile_rows + rl;
+    const int64_t base =
+        ((int64_t)h * p.n_pvt + (vt_first(t, p.n_qtiles, p.n_splits, p.n_splits_text) - p.part_vt0)) *
+            p.tile_rows + rl;
     float m = -INFINITY;
-    for (int sp = 0; sp < p.n_splits; ++sp) m = fmaxf(m, p.part_lse[base + (int64_t)sp * p.tile_rows]);
+    for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, p.part_lse[base + (int64_t)sp * p.tile_rows]);
     float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     float wsum = 0.0f;
     if (m != -INFINITY) {
-      for (int sp = 0; sp < p.n_splits; ++sp) {
+      for (int sp = 0; sp < n_split; ++sp) {
         const int64_t pr = base + (int64_t)sp * p.tile_rows;
         const float w = expf(p.part_lse[pr] - m);
         const float4 v = *reinterpret_cast<const float4*>(p.part_o + pr * D + 4 * d4);

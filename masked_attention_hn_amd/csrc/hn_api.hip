@@ -114,6 +114,20 @@ int choose_splits(int H, int n_qtiles, int64_t keys_per_tile) {
   return (int)std::max<int64_t>(sp, 1);
 }
 
+// Key splits per text query tile.  The text tiles of a joint launch come
+// after all video tiles and add a fraction of a round of blocks (the 480x832
+// segment: 80 text tasks after 736 video tasks on 256 CUs); in quarters they
+// fill the last round instead of adding one.  Text tiles with fewer than
+// 4096 keys are not split.  HN_ATTN_TEXT_SPLITS=n forces n.
+int choose_text_splits(int64_t text_tiles, int64_t keys_per_tile) {
+  if (const char* e = std::getenv("HN_ATTN_TEXT_SPLITS")) {
+    const int v = std::atoi(e);
+    if (v >= 1 && v <= HN_MAX_SPLITS) return v;
+  }
+  if (text_tiles <= 0 || keys_per_tile < 4096) return 1;
+  return 4;
+}
+
 // Query rows per tile of a plan: keep lists fix HN_TILE; dense plans use the
 // kernel's 256-row blocks (faster than 128-row ones even where 256-row blocks
 // leave compute units idle: the 2-head share above runs 1.386 ms with 208
@@ -168,6 +182,8 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     int64_t video = (int64_t)pp->ring_tokens + lq;
     if (sp && sp->row_ptr && pp->n_qtiles > 0) video = video / 4;
     pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video);
+    // text queries see heads, the whole ring and the own video (no keep list)
+    pp->n_splits_text = choose_text_splits(pp->n_text_tiles, keys + (int64_t)pp->ring_tokens + lq);
   }
   int max_spans = 4 + s->num_actions;
   if (sp) {
@@ -187,10 +203,30 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   return HN_OK;
 }
 
-int plan_vt(const hn::PlanParams& pp) { return (pp.n_qtiles + pp.n_text_tiles) * pp.n_splits; }
+int plan_vt(const hn::PlanParams& pp) {
+  return hn::vt_count(pp.n_qtiles, pp.n_text_tiles, pp.n_splits, pp.n_splits_text);
+}
+
+// Virtual tiles with a partial-result slot: [part_vt0, n_vt) -- every one when
+// video tiles are split, the text tiles when only they are, none otherwise.
+void plan_partials(int n_qtiles, int n_text_tiles, int ns, int nst, int* part_vt0, int* n_pvt) {
+  const int n_vt = hn::vt_count(n_qtiles, n_text_tiles, ns, nst);
+  if (ns > 1) {
+    *part_vt0 = 0;
+    *n_pvt = n_vt;
+  } else if (nst > 1 && n_text_tiles > 0) {
+    *part_vt0 = n_qtiles;
+    *n_pvt = n_vt - n_qtiles;
+  } else {
+    *part_vt0 = n_vt;
+    *n_pvt = 0;
+  }
+}
 
 size_t plan_ws_bytes(const hn_kv_cache* c, const hn::PlanParams& pp) {
-  return hn::plan_bytes(c->num_heads, plan_vt(pp), pp.max_spans, pp.tile_q, pp.n_splits);
+  int v0 = 0, np = 0;
+  plan_partials(pp.n_qtiles, pp.n_text_tiles, pp.n_splits, pp.n_splits_text, &v0, &np);
+  return hn::plan_bytes(c->num_heads, plan_vt(pp), pp.max_spans, pp.tile_q, np);
 }
 
 hn_status hip_fail(hipError_t e, const char* what) {
@@ -412,6 +448,8 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
     plan->frames_seen = c->frames_seen;
     plan->sparse = pp.sparse;
     plan->n_splits = pp.n_splits;
+    plan->n_splits_text = pp.n_splits_text;
+    plan->reserved0 = 0;
     {
       // text queries: every text row sees heads, ring, own head and own
       // video; a tail row also sees its own tail
@@ -475,7 +513,8 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
       plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
       plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile) ||
-      plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS)
+      plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS || plan->n_splits_text < 1 ||
+      plan->n_splits_text > HN_MAX_SPLITS)
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
@@ -498,8 +537,13 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.lq_txt = (int32_t)tl;
   p.n_qtiles = plan->n_qtiles;
   p.n_splits = plan->n_splits;
-  p.n_vt = (plan->n_qtiles + plan->n_text_tiles) * plan->n_splits;
-  p.n_tiles = (plan->n_qtiles + (text_q ? plan->n_text_tiles : 0)) * plan->n_splits;
+  p.n_splits_text = plan->n_splits_text;
+  p.n_vt = hn::vt_count(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text);
+  p.n_tiles = hn::vt_count(plan->n_qtiles, text_q ? plan->n_text_tiles : 0, plan->n_splits, plan->n_splits_text);
+  // partial results exist iff some launched tile is split
+  const bool partials = plan->n_splits > 1 || (text_q && plan->n_splits_text > 1);
+  plan_partials(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text, &p.part_vt0,
+                &p.n_pvt);
   p.tile_rows = plan->tile_q;
   p.max_spans = plan->max_spans;
   p.n_tasks = p.H * p.n_tiles;
@@ -511,11 +555,11 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.counts = static_cast<const int32_t*>(plan->dev);
   p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
                                               hn::plan_counts_bytes(p.n_vt));
-  if (p.n_splits > 1) {
+  if (p.n_pvt > 0) {
     char* base = const_cast<char*>(static_cast<const char*>(plan->dev)) +
                  hn::align256(hn::plan_spans_bytes(p.n_vt, plan->max_spans));
     p.part_o = reinterpret_cast<float*>(base);
-    p.part_lse = reinterpret_cast<float*>(base + hn::plan_partial_o_bytes(p.H, p.n_vt, plan->tile_q));
+    p.part_lse = reinterpret_cast<float*>(base + hn::plan_partial_o_bytes(p.H, p.n_pvt, plan->tile_q));
   }
   p.q = static_cast<const __bf16*>(q_vid);
   p.q_txt = text_q ? static_cast<const __bf16*>(q_txt) : nullptr;
@@ -531,15 +575,17 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.lse_txt = text_q ? lse_txt : nullptr;
   hipError_t e = hn::launch_attn(p, stream);
   if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (p.n_splits > 1) {
+  if (partials) {
     hn::MergeParams m;
     std::memset(&m, 0, sizeof(m));
     m.H = p.H;
     m.n_splits = p.n_splits;
-    m.n_vt = p.n_vt;
+    m.n_splits_text = p.n_splits_text;
+    m.part_vt0 = p.part_vt0;
+    m.n_pvt = p.n_pvt;
     m.tile_rows = plan->tile_q;
     m.n_qtiles = plan->n_qtiles;
-    m.n_tiles = p.n_tiles / p.n_splits;
+    m.n_tiles = plan->n_qtiles + (text_q ? plan->n_text_tiles : 0);
     m.lq = lq;
     m.lq_txt = (int32_t)tl;
     m.part_o = p.part_o;

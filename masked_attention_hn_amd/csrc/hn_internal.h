@@ -35,7 +35,8 @@ static_assert(sizeof(Span) == 32, "Span layout");
 struct PlanParams {
   int32_t n_qtiles;      // video query tiles
   int32_t n_text_tiles;  // text query tiles, after the video tiles
-  int32_t n_splits;      // key-range splits per query tile (split-KV); 1 = none
+  int32_t n_splits;      // key-range splits per video query tile (split-KV); 1 = none
+  int32_t n_splits_text; // key-range splits per text query tile
   int32_t tile_q;
   int32_t lq;            // F*P video queries
   int32_t P;
@@ -62,7 +63,9 @@ struct PlanParams {
 // Workspace layout of a tile plan over n_vt virtual tiles (query tile x key
 // split, split fastest): int32 count[n_vt] padded to 256 bytes, then
 // Span spans[n_vt][max_spans]; with splits, then (256-byte aligned) the
-// partial results float o[H][n_vt][rows][D] and float lse[H][n_vt][rows].
+// partial results float o[H][n_pvt][rows][D] and float lse[H][n_pvt][rows]
+// of the n_pvt virtual tiles from part_vt0 on (every virtual tile when video
+// tiles are split, else only the text tiles).
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t plan_counts_bytes(int n_vt) { return align256((size_t)n_vt * sizeof(int32_t)); }
 inline size_t plan_spans_bytes(int n_vt, int max_spans) {
@@ -74,10 +77,32 @@ inline size_t plan_partial_o_bytes(int H, int n_vt, int rows) {
 inline size_t plan_partial_lse_bytes(int H, int n_vt, int rows) {
   return align256((size_t)H * n_vt * rows * sizeof(float));
 }
-inline size_t plan_bytes(int H, int n_vt, int max_spans, int rows, int n_splits) {
+inline size_t plan_bytes(int H, int n_vt, int max_spans, int rows, int n_pvt) {
   size_t b = align256(plan_spans_bytes(n_vt, max_spans));
-  if (n_splits > 1) b += plan_partial_o_bytes(H, n_vt, rows) + plan_partial_lse_bytes(H, n_vt, rows);
+  if (n_pvt > 0) b += plan_partial_o_bytes(H, n_pvt, rows) + plan_partial_lse_bytes(H, n_pvt, rows);
   return b;
+}
+
+// Virtual tiles: every video query tile split ns ways, then every text query
+// tile split nst ways, split index fastest.
+__host__ __device__ inline int vt_count(int n_qtiles, int n_text_tiles, int ns, int nst) {
+  return n_qtiles * ns + n_text_tiles * nst;
+}
+__host__ __device__ inline int vt_first(int tile, int n_qtiles, int ns, int nst) {
+  return tile < n_qtiles ? tile * ns : n_qtiles * ns + (tile - n_qtiles) * nst;
+}
+__host__ __device__ inline void vt_decode(int vt, int n_qtiles, int ns, int nst, int& tile, int& split,
+                                          int& n_split) {
+  if (vt < n_qtiles * ns) {
+    tile = vt / ns;
+    split = vt - tile * ns;
+    n_split = ns;
+  } else {
+    const int r = vt - n_qtiles * ns;
+    tile = n_qtiles + r / nst;
+    split = r - (r / nst) * nst;
+    n_split = nst;
+  }
 }
 
 struct AttnParams {
@@ -85,8 +110,11 @@ struct AttnParams {
   int32_t lq;            // video query rows
   int32_t n_qtiles;      // video query tiles
   int32_t n_tiles;       // virtual tiles per head this launch covers (video, then text if any)
-  int32_t n_splits;      // key splits per query tile; > 1: write partials, merge after
-  int32_t n_vt;          // virtual tiles per head in the plan (partial-buffer stride)
+  int32_t n_splits;      // key splits per video query tile; > 1: write partials, merge after
+  int32_t n_splits_text; // key splits per text query tile
+  int32_t n_vt;          // virtual tiles per head in the plan
+  int32_t part_vt0;      // first virtual tile with a partial-result slot
+  int32_t n_pvt;         // partial-result slots per head
   int32_t lq_txt;        // text query rows
   int32_t tile_rows;     // query rows per plan tile (selects the kernel instance)
   int32_t max_spans;
@@ -116,7 +144,7 @@ struct AttnParams {
   __bf16* o_txt;
   float* lse;
   float* lse_txt;
-  float* part_o;         // [H][n_vt][tile_rows][D] when n_splits > 1
+  float* part_o;         // [H][n_vt][tile_rows][D] when any tile is split
   float* part_lse;       // [H][n_vt][tile_rows]
 };
 
@@ -124,7 +152,9 @@ struct AttnParams {
 struct MergeParams {
   int32_t H;
   int32_t n_splits;
-  int32_t n_vt;          // virtual tiles per head in the plan
+  int32_t n_splits_text;
+  int32_t part_vt0;      // first virtual tile with a partial-result slot
+  int32_t n_pvt;         // partial-result slots per head
   int32_t tile_rows;
   int32_t n_qtiles;      // video query tiles
   int32_t n_tiles;       // query tiles merged (video, then text if any)

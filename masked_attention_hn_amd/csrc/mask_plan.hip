@@ -25,8 +25,9 @@
 // and they attend densely (keep lists concern video query tiles): at most
 // 4 + m spans as well.
 //
-// Split-KV: with n_splits > 1 every query tile becomes n_splits virtual tiles
-// (split fastest), each the same span list clipped to one contiguous range
+// Split-KV: with n_splits > 1 every video query tile (n_splits_text > 1: every
+// text query tile) becomes that many virtual tiles (split fastest), each the
+// same span list clipped to one contiguous range
 // of its keys in visiting order, with range boundaries on multiples of 64
 // keys; the attention kernel writes partial results for each and a merge
 // kernel combines them.
@@ -163,14 +164,14 @@ __device__ int64_t split_bound(int64_t total, int i, int n) {
 
 // Span list of virtual tile vt = (query tile, key split).
 __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
-  const int qt = vt / p.n_splits;
-  const int split = vt - qt * p.n_splits;
+  int qt, split, n_split;
+  vt_decode(vt, p.n_qtiles, p.n_splits, p.n_splits_text, qt, split, n_split);
   const int n = build_tile_spans(p, qt, out);
-  if (p.n_splits == 1) return n;
+  if (n_split == 1) return n;
   int64_t total = 0;
   for (int i = 0; i < n; ++i) total += out[i].k1 - out[i].k0;
-  const int64_t a = split_bound(total, split, p.n_splits);
-  const int64_t b = split_bound(total, split + 1, p.n_splits);
+  const int64_t a = split_bound(total, split, n_split);
+  const int64_t b = split_bound(total, split + 1, n_split);
   // clip in place (entry m <= i is written only after entry i was read)
   int m = 0;
   int64_t pos = 0;
@@ -191,7 +192,7 @@ __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
 
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
   const int vt = blockIdx.x * 64 + threadIdx.x;
-  if (vt >= (p.n_qtiles + p.n_text_tiles) * p.n_splits) return;
+  if (vt >= vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text)) return;
   counts[vt] = build_spans(p, vt, spans + (int64_t)vt * p.max_spans);
 }
 
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
 
 hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
-  const int n_vt = (p.n_qtiles + p.n_text_tiles) * p.n_splits;
+  const int n_vt = vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text);
   Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(n_vt));
   const int blocks = (n_vt + 63) / 64;
   hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(64), 0, s, p, counts, spans);

@@ -114,7 +114,7 @@ def test_attention_rejects_stale_plan():
     c = fake_cache()
     s = seg_c()
     plan = hn.hn_tile_plan(dev=FAKE, tile_q=128, n_qtiles=1, n_text_tiles=1, max_spans=6,
-                           n_splits=1, visible_pairs=-1)
+                           n_splits=1, n_splits_text=1, visible_pairs=-1)
     fwd = hn._lib.hn_seg_attn_fwd
     q = [FAKE, None]                # q_vid, q_txt
     kv = [FAKE] * 4                 # k_txt, v_txt, k_vid, v_vid
@@ -140,6 +140,9 @@ def test_attention_rejects_stale_plan():
     plan.n_splits = 0              # not a plan the builder writes
     assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
     plan.n_splits = 1
+    plan.n_splits_text = 17
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.n_splits_text = 1
     assert call(s, None) == hn.HN_ERR_NULL
     assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID
     assert call(s, ctypes.byref(plan), scale=-0.1) == hn.HN_ERR_INVALID   # positive scales only
@@ -166,7 +169,7 @@ def test_split_count_forced_and_sized(monkeypatch):
     n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
     monkeypatch.setenv("HN_ATTN_SPLITS", "3")
     n3 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
-    vt = 2 * 3                                 # (video + text tile) x 3 splits
+    vt = 1 * 3 + 1 * 1                         # video tile x 3 splits + text tile (80 keys: unsplit)
     spans = -(-(256 + vt * 6 * 32) // 256) * 256
     a256 = lambda b: -(-b // 256) * 256
     # partials for the dense plans' query-tile height R (the kernel's choice)
@@ -182,6 +185,7 @@ def test_automatic_split_only_for_small_grids(monkeypatch):
     blocks is not split; a 1-head layout with 2 query tiles of long key lists
     is split to about two blocks per CU, capped at 16 and at 1024 keys per split."""
     monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
+    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "1")   # video tiles only here
     plan_sizes = {}
     for H, P, frames, W_ in ((16, 390, 30, 1), (1, 128, 2, 200)):
         c = fake_cache(H=H, P=P, W=W_)
@@ -196,7 +200,7 @@ def test_automatic_split_only_for_small_grids(monkeypatch):
     a256 = lambda b: -(-b // 256) * 256
     ok = []
     for R in (128, 256):
-        n_vt = (-(-256 // R) + 1) * 16
+        n_vt = -(-256 // R) * 16 + 1        # video tiles x 16 splits + the (unsplit) text tile
         spans = a256(a256(n_vt * 4) + n_vt * 4 * 32)
         ok.append(plan_sizes[1] == spans + a256(n_vt * R * 128 * 4) + a256(n_vt * R * 4))
     assert any(ok)
@@ -261,7 +265,7 @@ def test_attention_rejects_sources_over_2gib():
     fwd = hn._lib.hn_seg_attn_fwd
     for rows in (128, 256):
         plan = hn.hn_tile_plan(dev=FAKE, tile_q=rows, n_qtiles=-(-F * P // rows), n_text_tiles=0,
-                               max_spans=4, n_splits=1, visible_pairs=-1)
+                               max_spans=4, n_splits=1, n_splits_text=1, visible_pairs=-1)
         st = fwd(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(plan), FAKE, None, None, None,
                  FAKE, FAKE, FAKE, None, None, None, 0.1, None)
         if st != hn.HN_ERR_ORDER:          # the plan height the library uses
@@ -269,3 +273,20 @@ def test_attention_rejects_sources_over_2gib():
             break
     else:
         raise AssertionError("no plan height accepted")
+
+
+def test_text_tiles_split_separately(monkeypatch):
+    """Text query tiles get their own split count: forced to 4 with video tiles
+    unsplit, the partial results cover only the text tiles."""
+    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
+    c = fake_cache()
+    s = seg_c()
+    n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "4")
+    n4 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    a256 = lambda b: -(-b // 256) * 256
+    vt = 1 + 4                                 # video tile unsplit + text tile x 4
+    spans = a256(a256(vt * 4) + vt * 6 * 32)
+    fits = [R for R in (64, 128, 256, 512)
+            if n4 == spans + a256(2 * 4 * R * 128 * 4) + a256(2 * 4 * R * 4)]   # 4 text slots per head
+    assert len(fits) == 1 and n4 > n1

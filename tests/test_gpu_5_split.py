@@ -41,16 +41,18 @@ def _bar(w, got, ref):
     return err
 
 
-@pytest.mark.parametrize("name,splits", [("c1", 3), ("c1", 16), ("c1_evict", 2), ("m1", 5),
-                                         ("m2", 4), ("m3", 3), ("m4", 7)])
-def test_forced_splits(name, splits, monkeypatch):
-    print(f"[split] {name} x{splits}", flush=True)
+@pytest.mark.parametrize("name,splits,text_splits", [("c1", 3, 1), ("c1", 16, 16), ("c1_evict", 2, 3),
+                                                     ("m1", 5, 1), ("m1", 1, 4), ("m2", 4, 2),
+                                                     ("m3", 3, 1), ("m4", 7, 5), ("m4", 1, 3)])
+def test_forced_splits(name, splits, text_splits, monkeypatch):
+    print(f"[split] {name} x{splits} text x{text_splits}", flush=True)
     monkeypatch.setenv("HN_ATTN_SPLITS", str(splits))
+    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", str(text_splits))
     w = W.config(name)
     d = data_of(name)
     run = G.Run(w, d)
-    assert run.plan.c.n_splits == splits
-    if w.current.text_len > 0 and w.sparse_keep is None:
+    assert run.plan.c.n_splits == splits and run.plan.c.n_splits_text == text_splits
+    if w.current.text_len > 0:
         o, o_txt, lse, lse_txt = run.attn_joint()
         rows_t = np.arange(w.current.text_len)
         ref_t, ref_lse_t, _ = oracle.attention(w, d, rows_t, queries="text")
@@ -64,7 +66,9 @@ def test_forced_splits(name, splits, monkeypatch):
     print(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
     assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-2
     # deterministic: the same call again gives the same bits
-    o2 = run.attn()[0] if not (w.current.text_len > 0 and w.sparse_keep is None) else run.attn_joint()[0]
+    o2 = run.attn_joint()[0] if w.current.text_len > 0 else run.attn()[0]
+    # and the video-only call (text tiles planned but not launched) agrees bit for bit
+    assert torch.equal(run.attn()[0], o)
     assert torch.equal(o, o2)
 
 
