@@ -10,39 +10,45 @@
 //
 // HBM-bound: per (token, head) it reads the 256-byte query and writes the
 // 256-byte output (+ 4 bytes of lse); the camera keys and values (F x H x 256
-// bytes each) stay in cache.  8 lanes own one row (16 values each, 32-byte
-// loads and stores); the score is an 8-lane butterfly; online softmax over
-// the visible camera tokens in fp32.
+// bytes each) stay in cache.  16 lanes own one row (8 values each, one
+// 16-byte load and store; measured 8% faster than 8 lanes x 32 bytes, and
+// 4 lanes x 64 bytes slower still); the score is a 16-lane butterfly; online
+// softmax over the visible camera tokens in fp32.
 #include "hn_internal.h"
 
 namespace hn {
 namespace {
 
-constexpr int LANES = 8;            // lanes per (token, head) row
+constexpr int LANES = 16;            // lanes per (token, head) row
 constexpr int ROWS = 256 / LANES;   // rows per block
 
-__device__ inline void load16(const __bf16* p, float (&x)[16]) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 8);
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+constexpr int E = 8;
+// E consecutive bf16 values -> float
+__device__ inline void load_row(const __bf16* p, float (&x)[E]) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    x[2 * i] = __uint_as_float(w[i] << 16);
-    x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+  for (int c = 0; c < E / 8; ++c) {
+    const uint4 a = *reinterpret_cast<const uint4*>(p + 8 * c);
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * c + 2 * i] = __uint_as_float(w[i] << 16);
+      x[8 * c + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+    }
   }
 }
 
-__device__ inline float sum8(float x) {
+__device__ inline float sum_lanes(float x) {
   x += __shfl_xor(x, 1);
   x += __shfl_xor(x, 2);
   x += __shfl_xor(x, 4);
+  x += __shfl_xor(x, 8);
   return x;
 }
 
 __global__ __launch_bounds__(256) void camera_attn_kernel(CameraParams p) {
   const int lane = threadIdx.x & (LANES - 1);
   const int64_t unit = (int64_t)blockIdx.x * ROWS + (threadIdx.x / LANES);
-  // whole 8-lane groups leave together, so the butterflies stay inside active lanes
+  // whole lane groups leave together, so the butterflies stay inside active lanes
   if (unit >= p.rows * p.H) return;
   const int64_t t = unit / p.H;
   const int h = (int)(unit - t * p.H);
@@ -50,40 +56,41 @@ __global__ __launch_bounds__(256) void camera_attn_kernel(CameraParams p) {
   const int lo = max(0, f - p.radius);
   const int hi = min(p.F, f + p.radius + 1);
 
-  float q[16];
-  load16(p.q + (t * p.H + h) * D + lane * 16, q);
+  float q[E];
+  load_row(p.q + (t * p.H + h) * D + lane * E, q);
   float m = -INFINITY, l = 0.0f;
-  float acc[16];
+  float acc[E];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+  for (int i = 0; i < E; ++i) acc[i] = 0.0f;
   for (int g = lo; g < hi; ++g) {
-    const int64_t kv = ((int64_t)g * p.H + h) * D + lane * 16;
-    float k[16];
-    load16(p.k + kv, k);
+    const int64_t kv = ((int64_t)g * p.H + h) * D + lane * E;
+    float k[E];
+    load_row(p.k + kv, k);
     float s = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s = __builtin_fmaf(q[i], k[i], s);
-    s = sum8(s) * p.scale_log2;
+    for (int i = 0; i < E; ++i) s = __builtin_fmaf(q[i], k[i], s);
+    s = sum_lanes(s) * p.scale_log2;
     const float m_new = fmaxf(m, s);
     const float alpha = __builtin_amdgcn_exp2f(m - m_new);
     const float w = __builtin_amdgcn_exp2f(s - m_new);
-    float v[16];
-    load16(p.v + kv, v);
+    float v[E];
+    load_row(p.v + kv, v);
     l = l * alpha + w;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = acc[i] * alpha + w * v[i];
+    for (int i = 0; i < E; ++i) acc[i] = acc[i] * alpha + w * v[i];
     m = m_new;
   }
   const float inv = l > 0.0f ? 1.0f / l : 0.0f;
-  uint32_t o[8];
+  uint32_t o[E / 2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < E / 2; ++i) {
     const bf16x2_t pr = {(__bf16)(acc[2 * i] * inv), (__bf16)(acc[2 * i + 1] * inv)};
     o[i] = __builtin_bit_cast(uint32_t, pr);
   }
-  __bf16* dst = p.o + (t * p.H + h) * D + lane * 16;
-  *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
-  *reinterpret_cast<uint4*>(dst + 8) = make_uint4(o[4], o[5], o[6], o[7]);
+  __bf16* dst = p.o + (t * p.H + h) * D + lane * E;
+#pragma unroll
+  for (int c = 0; c < E / 8; ++c)
+    *reinterpret_cast<uint4*>(dst + 8 * c) = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
   if (p.lse != nullptr && lane == 0)
     p.lse[(int64_t)h * p.rows + t] = l > 0.0f ? (m + __log2f(l)) * 0.69314718055994530942f : -INFINITY;
 }
