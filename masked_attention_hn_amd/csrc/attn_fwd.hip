@@ -327,11 +327,15 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
 
   f32x16 s[QB][KB];
 #pragma unroll
-  for (int kb = 0; kb < KB; ++kb) {
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
     for (int q = 0; q < QB; ++q) s[q][kb] = f32x16{};
+  // consecutive MFMAs accumulate into different 32-key blocks, so none waits
+  // for the previous one's result
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+  for (int t = 0; t < 8; ++t) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
       const bf16x8 kk = ld8(kl + (kb * 8 + t) * 512);
 #pragma unroll
       for (int q = 0; q < QB; ++q)
@@ -404,10 +408,11 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
         }
       st[q].l = l;
     }
+    // consecutive MFMAs accumulate into different 32-column blocks of O
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int t = 0; t < 2; ++t) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int c = 0; c < 4; ++c) {
         const __bf16* a = vl + ((c * KB + kb) * 2 + t) * 512;
         const bf16x8 vv = tr_read8(a, a + 256);
 #pragma unroll
