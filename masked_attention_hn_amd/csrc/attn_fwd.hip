@@ -478,21 +478,27 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   const int n_spans = p.counts[vt];
   const Span* spans = p.spans + (int64_t)vt * p.max_spans;
 
-  // tile iterator over the spans (block-uniform)
+  // tile iterator over the spans (block-uniform).  The current span is kept in
+  // registers and the next one is read when a span ends, so the read is
+  // waited on one step later, behind that step's tile loads.
   int e = 0;
-  int kpos = n_spans > 0 ? spans[0].k0 : 0;
+  Span sp{};
+  if (n_spans > 0) sp = spans[0];
+  int kpos = sp.k0;
   auto next_tile = [&](TileDesc& t) __attribute__((always_inline)) -> bool {
     if (e >= n_spans) return false;
-    const Span s = spans[e];
-    t.src = s.src;
+    t.src = sp.src;
     t.kb = kpos;
-    t.nk = min(C::KT, s.k1 - kpos);
-    t.r0 = s.r0;
-    t.r1 = s.r1;
+    t.nk = min(C::KT, sp.k1 - kpos);
+    t.r0 = sp.r0;
+    t.r1 = sp.r1;
     kpos += t.nk;
-    if (kpos >= s.k1) {
+    if (kpos >= sp.k1) {
       ++e;
-      if (e < n_spans) kpos = spans[e].k0;
+      if (e < n_spans) {
+        sp = spans[e];
+        kpos = sp.k0;
+      }
     }
     return true;
   };
