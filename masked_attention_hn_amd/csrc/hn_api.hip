@@ -91,27 +91,39 @@ int device_cus() {
   return n;
 }
 
-// Key splits per query tile (split-KV).  Measured on MI355X, splitting does
-// not pay while the grid covers even half the compute units: the fp32
-// partial results plus the merge cost more than the better fill.  The 2-head
-// share of the 1280x704 steady state (208 blocks of 256 rows on 256 CUs)
-// takes 1.386 ms unsplit and 1.543 / 1.532 ms with 2 / 3 splits; with
-// 128-row blocks (414 blocks) 1.54 / 1.73 / 1.59 / 1.61 / 1.56 ms with
-// 1 / 2 / 3 / 4 / 8 splits.  So only a grid with at most one block per two
-// CUs is split, to about one block per CU, with no fewer than 1024 keys per
-// split.  HN_ATTN_SPLITS=n in the environment forces n (tuning and tests).
-int choose_splits(int H, int n_qtiles, int64_t keys_per_tile) {
+// Key splits per query tile (split-KV).  A split costs fp32 partial results,
+// a merge and one more first-tile latency per query tile: measured on MI355X
+// about a quarter of an unsplit task's time.  It pays where the grid leaves
+// the last round of blocks partly empty and half-length tasks fill it:
+//   1280x704 steady state, 16 heads: 1,664 blocks of 256 rows = 6.5 rounds on
+//     256 CUs; 1 / 2 / 3 splits 10.09 / 9.77 / 10.73 ms per launch, and the
+//     7th segment (158k INT8 history keys) 44.86 / 43.16 ms at 1 / 2;
+//   its 2-head share: 206 blocks, one round; 1 / 5 / 6 / 7 splits
+//     1.238 / 1.398 / 1.363 / 1.386 ms.
+// With r_s = rounds of the s-split grid, two splits are taken when
+// r_2 / 2 + 1/4 < r_1 and each half keeps at least 8192 keys.  A grid of at
+// most one block per two CUs is split to about one block per CU, with no
+// fewer than 1024 keys per split.  blocks_per_cu is how many blocks of the
+// plan's tile height share a CU.  HN_ATTN_SPLITS=n in the environment forces
+// n (tuning and tests).
+int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu) {
   if (const char* e = std::getenv("HN_ATTN_SPLITS")) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= HN_MAX_SPLITS) return v;
   }
   const int64_t cus = device_cus();
   const int64_t tasks = (int64_t)H * n_qtiles;
-  if (tasks <= 0 || 2 * tasks > cus) return 1;
-  int64_t sp = ceil_div(cus, tasks);
-  sp = std::min<int64_t>(sp, keys_per_tile / 1024);
-  sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
-  return (int)std::max<int64_t>(sp, 1);
+  if (tasks <= 0) return 1;
+  if (2 * tasks <= cus) {
+    int64_t sp = ceil_div(cus, tasks);
+    sp = std::min<int64_t>(sp, keys_per_tile / 1024);
+    sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
+    return (int)std::max<int64_t>(sp, 1);
+  }
+  const int64_t slots = cus * std::max(blocks_per_cu, 1);
+  const int64_t r1 = ceil_div(tasks, slots), r2 = ceil_div(2 * tasks, slots);
+  if (keys_per_tile >= 16384 && 2 * r2 + 1 < 4 * r1) return 2;
+  return 1;
 }
 
 // Key splits per text query tile.  The text tiles of a joint launch come
@@ -181,7 +193,8 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     int64_t keys = (int64_t)pp->head_tokens + tl;
     int64_t video = (int64_t)pp->ring_tokens + lq;
     if (sp && sp->row_ptr && pp->n_qtiles > 0) video = video / 4;
-    pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video);
+    // dense 256-row blocks run one per CU, 128-row blocks two
+    pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video, pp->tile_q >= 256 ? 1 : 2);
     // text queries see heads, the whole ring and the own video (no keep list)
     pp->n_splits_text = choose_text_splits(pp->n_text_tiles, keys + (int64_t)pp->ring_tokens + lq);
   }

@@ -181,9 +181,10 @@ def test_split_count_forced_and_sized(monkeypatch):
 
 
 def test_automatic_split_only_for_small_grids(monkeypatch):
-    """Without a device (256 compute units assumed) a grid of at least 256
-    blocks is not split; a 1-head layout with 2 query tiles of long key lists
-    is split to about two blocks per CU, capped at 16 and at 1024 keys per split."""
+    """Without a device (256 compute units assumed) a 16-head grid with short
+    key lists is not split; a 1-head layout with 2 query tiles of long key
+    lists is split to about two blocks per CU, capped at 16 and at 1024 keys
+    per split."""
     monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
     monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "1")   # video tiles only here
     plan_sizes = {}
@@ -204,6 +205,34 @@ def test_automatic_split_only_for_small_grids(monkeypatch):
         spans = a256(a256(n_vt * 4) + n_vt * 4 * 32)
         ok.append(plan_sizes[1] == spans + a256(n_vt * R * 128 * 4) + a256(n_vt * R * 4))
     assert any(ok)
+
+
+def test_automatic_two_splits_fill_the_last_round(monkeypatch):
+    """Without a device (256 compute units assumed): a 16-head grid whose last
+    round of blocks is half empty and whose query tiles visit >= 16,384 keys
+    (the 1280x704 steady state: 26,400 queries, 18-frame ring) is split in
+    two; the same grid with short key lists (the 480x832 segment), and the
+    2-head share (one round of blocks), are not.  The automatic workspace size
+    must equal the one of the forced split count."""
+    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "1")
+
+    def ws(H, P, frames, W_, splits=None):
+        if splits is None:
+            monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
+        else:
+            monkeypatch.setenv("HN_ATTN_SPLITS", str(splits))
+        c = fake_cache(H=H, P=P, W=W_)
+        c.frames_seen = W_          # a full ring of history
+        c.segments = 0
+        seg = hn.SegLayout(0, frames, P, 16, [], [], [])
+        return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+
+    steady = (16, 880, 30, 18)       # 1,664 blocks of 256 rows: 6.5 rounds
+    assert ws(*steady) == ws(*steady, splits=2) != ws(*steady, splits=1)
+    short = (16, 390, 30, 1)         # 12,106 keys per query tile
+    assert ws(*short) == ws(*short, splits=1)
+    share = (2, 880, 30, 18)         # 206 blocks: one round either way
+    assert ws(*share) == ws(*share, splits=1)
 
 
 def test_archive_checks():
