@@ -10,7 +10,9 @@
 //            QB blocks of 32 query rows.  Every K/V operand a wave reads from
 //            LDS feeds QB MFMAs; QB = 2 would halve the LDS traffic per flop
 //            but needs more than 256 VGPRs (one wave per SIMD), which measured
-//            slower, so the instances below use QB = 1 and two blocks per CU.
+//            slower, so the instances below use QB = 1: 8 waves x 32 rows, one
+//            block per CU, for dense plans; 4 waves x 32 rows, two blocks per
+//            CU, for keep-list plans (the keep list's 128-row query tile).
 //   tile   = KT keys of one span of the tile plan, staged in LDS as bf16 in
 //            operand-major order, so that every MFMA operand a wave reads is
 //            64 consecutive slots (conflict-free); the V^T operand of the PV
