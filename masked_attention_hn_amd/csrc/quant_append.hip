@@ -13,7 +13,9 @@
 // lane writes 16 int8 codes (one 16-byte store) per tensor.  Consecutive
 // 8-lane groups take the heads of one token, so each wave reads 8 x 256
 // contiguous bytes per tensor.  (16-byte stores measured 9-13% faster than
-// 8-byte ones; non-temporal loads/stores and two rows per lane group slower.)
+// 8-byte ones; non-temporal loads/stores, two rows per lane group, and blocks
+// of 32 consecutive tokens of one head, which write their codes and scales
+// contiguously but read rows 4 KB apart, were slower: the last by 10%.)
 // The division is the compiler's correctly rounded fp32 divide (no fast-math);
 // fp32 denormals are preserved so subnormal scales quantize exactly.
 #include "hn_internal.h"
