@@ -98,7 +98,7 @@ int device_cus() {
 //   1280x704 steady state, 16 heads: 1,664 blocks of 256 rows = 6.5 rounds on
 //     256 CUs; 1 / 2 / 3 splits 10.09 / 9.77 / 10.73 ms per launch, and the
 //     7th segment (158k INT8 history keys) 44.86 / 43.16 ms at 1 / 2;
-//   its 2-head share: 206 blocks, one round; 1 / 5 / 6 / 7 splits
+//   its 2-head share: 208 blocks, one round; 1 / 5 / 6 / 7 splits
 //     1.238 / 1.398 / 1.363 / 1.386 ms.
 // With r_s = rounds of the s-split grid, two splits are taken when
 // r_2 / 2 + 1/4 < r_1 and each half keeps at least 8192 keys.  A grid of at

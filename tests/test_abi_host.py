@@ -231,7 +231,7 @@ def test_automatic_two_splits_fill_the_last_round(monkeypatch):
     assert ws(*steady) == ws(*steady, splits=2) != ws(*steady, splits=1)
     short = (16, 390, 30, 1)         # 12,106 keys per query tile
     assert ws(*short) == ws(*short, splits=1)
-    share = (2, 880, 30, 18)         # 206 blocks: one round either way
+    share = (2, 880, 30, 18)         # 208 blocks: one round either way
     assert ws(*share) == ws(*share, splits=1)
 
 
