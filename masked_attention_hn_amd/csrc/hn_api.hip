@@ -348,6 +348,9 @@ hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void*
                 c->head_cap_tokens, s->head_len);
   const int P = c->tokens_per_frame;
   const int surv = std::min(s->frames, c->window_frames);
+  if (((int64_t)s->head_len + (int64_t)surv * P) * c->num_heads >= (int64_t(1) << 31))
+    return fail(HN_ERR_UNSUPPORTED, "segment of %d head + %d video tokens x %d heads: 2^31 rows or more",
+                s->head_len, surv * P, c->num_heads);
   hn::AppendParams p;
   std::memset(&p, 0, sizeof(p));
   p.H = c->num_heads;

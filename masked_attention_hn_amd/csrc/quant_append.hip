@@ -16,8 +16,14 @@
 // 8-byte ones; non-temporal loads/stores, two rows per lane group, and blocks
 // of 32 consecutive tokens of one head, which write their codes and scales
 // contiguously but read rows 4 KB apart, were slower: the last by 10%.)
-// The division is the compiler's correctly rounded fp32 divide (no fast-math);
-// fp32 denormals are preserved so subnormal scales quantize exactly.
+// The quotient is taken as x * rcp(scale) and rounded; only where that
+// product lies within 2^-13 of a half-integer (where it could round apart
+// from the correctly rounded quotient), and for zero, tiny, huge or
+// non-finite scales, does a group of 8 values take the compiler's correctly
+// rounded fp32 divide (no fast-math).  This cut the VALU work about 3x: +10%
+// on the 1280x704 segment's append, +4% on the six-segment history, no
+// change on the 480x832 segment, whose short launch is latency-bound.  fp32
+// denormals are preserved so subnormal scales quantize exactly.
 #include "hn_internal.h"
 
 namespace hn {
@@ -39,6 +45,37 @@ __device__ inline uint2 quant8(const float (&x)[8], float scale, bool zero) {
   r.x = b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24);
   r.y = b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24);
   return r;
+}
+
+// Fast path for 8 values of a row with a normal scale: y = x * rcp(scale)
+// is within 3.1e-5 of the correctly rounded quotient fl(x / scale) when
+// |y| <= 127.0001 (reciprocal within 1 ulp, product rounded, quotient rounded),
+// so rint(y) == rint(fl(x / scale)) unless y lies within 2^-13 of a
+// half-integer.  Returns false if some value is that close; the caller then
+// takes the exact quotient for the 8 values.  Codes are packed as q + 128
+// (an exact integer in [1, 255]) and turned into two's complement bytes by
+// flipping bit 7.
+__device__ inline bool quant8_fast(const float (&x)[8], float r, uint2& out) {
+  float far = 0.0f;  // largest |y - rint(y)|
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float y = x[i] * r;
+    const float q = __builtin_rintf(y);
+    far = fmaxf(far, fabsf(y - q));
+    w[i / 4] = __builtin_amdgcn_cvt_pk_u8_f32(q + 128.0f, i % 4, w[i / 4]);
+  }
+  out.x = w[0] ^ 0x80808080u;
+  out.y = w[1] ^ 0x80808080u;
+  return far <= 0.5f - 0x1p-13f;
+}
+
+// Codes of 8 values with the given scale; fast is false for a zero,
+// subnormal-range or non-finite scale, which always take the exact quotient.
+__device__ inline uint2 quant8_any(const float (&x)[8], float scale, float r, bool fast, bool zero) {
+  uint2 q;
+  if (fast && quant8_fast(x, r, q)) return q;
+  return quant8(x, scale, zero);
 }
 
 __device__ inline void unpack8(uint4 w, float (&x)[8], float& amax) {
@@ -66,8 +103,10 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
   // Whole 8-lane groups leave together, so the butterflies below stay inside
   // active lanes.
   if (unit >= rows * p.H) return;
-  const int t = (int)(unit / p.H);
-  const int h = (int)(unit - (int64_t)t * p.H);
+  // units stay below 2^31 (the host checks), so 32-bit division suffices
+  const uint32_t u32 = (uint32_t)unit;
+  const int t = (int)(u32 / (uint32_t)p.H);
+  const int h = (int)(u32 - (uint32_t)t * (uint32_t)p.H);
 
   const __bf16 *ks, *vs;
   int8_t *kd, *vd;
@@ -103,8 +142,15 @@ __global__ __launch_bounds__(256) void quant_append_kernel(AppendParams p) {
   const float va = row_amax8(fmaxf(va0, va1));
   const float ksc = ka / 127.0f;
   const float vsc = va / 127.0f;
-  const uint2 kq0 = quant8(kx0, ksc, ka == 0.0f), kq1 = quant8(kx1, ksc, ka == 0.0f);
-  const uint2 vq0 = quant8(vx0, vsc, va == 0.0f), vq1 = quant8(vx1, vsc, va == 0.0f);
+  // a reciprocal within 1 ulp needs a normal, finite scale well inside range
+  const bool kfast = ksc >= 0x1p-100f && ksc <= 0x1p100f;
+  const bool vfast = vsc >= 0x1p-100f && vsc <= 0x1p100f;
+  const float kr = __builtin_amdgcn_rcpf(kfast ? ksc : 1.0f);
+  const float vr = __builtin_amdgcn_rcpf(vfast ? vsc : 1.0f);
+  const uint2 kq0 = quant8_any(kx0, ksc, kr, kfast, ka == 0.0f);
+  const uint2 kq1 = quant8_any(kx1, ksc, kr, kfast, ka == 0.0f);
+  const uint2 vq0 = quant8_any(vx0, vsc, vr, vfast, va == 0.0f);
+  const uint2 vq1 = quant8_any(vx1, vsc, vr, vfast, va == 0.0f);
 
   *reinterpret_cast<uint4*>(kd + dst_row * D + lane8 * 16) = make_uint4(kq0.x, kq0.y, kq1.x, kq1.y);
   *reinterpret_cast<uint4*>(vd + dst_row * D + lane8 * 16) = make_uint4(vq0.x, vq0.y, vq1.x, vq1.y);
