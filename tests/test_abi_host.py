@@ -70,6 +70,22 @@ def test_append_validation():
     assert call_append(z, seg_c()) == hn.HN_ERR_NULL
 
 
+def test_append_rejects_2pow31_rows():
+    """The quantize/append kernel indexes (token, head) rows in 32 bits: a
+    segment with 2^31 or more surviving rows is refused before any launch;
+    without a device, one just below the bound gets past that check (and
+    fails at the launch instead)."""
+    H, P, F = 16, 4096, 32768                    # 16 x 4096 x 32768 = 2^31 rows
+    c = fake_cache(H=H, P=P, W=F, cap=0)
+    s = hn.SegLayout(0, F, P, 0, [], [], [])
+    assert call_append(c, s) == hn.HN_ERR_UNSUPPORTED
+    assert "2^31" in hn.hn_last_error()
+    assert (c.frames_seen, c.head_tokens, c.segments) == (0, 0, 0)
+    if not torch.cuda.is_available():           # the fake pointers must never reach a GPU
+        small = hn.SegLayout(0, F - 1, P, 0, [], [], [])
+        assert call_append(fake_cache(H=H, P=P, W=F, cap=0), small) == hn.HN_ERR_HIP
+
+
 @pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device failure path")
 def test_failed_launch_leaves_cache_unchanged():
     c = fake_cache()
