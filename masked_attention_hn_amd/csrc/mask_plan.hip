@@ -38,31 +38,57 @@
 namespace hn {
 namespace {
 
+// Emits one query tile's spans in visiting order.  The last span is held in
+// registers until the next one cannot extend it, so nothing written is read
+// back (a store followed by a load of the same address costs a memory round
+// trip per span).  With a clip window [lo, hi) (split-KV) each span is cut to
+// the part of the window it covers, counting keys in visiting order; the
+// writer also counts the keys of all spans (out may be null to count only).
 struct SpanWriter {
   Span* out;
   int n;
   int cap;
-  int R0, R1;  // rows of the query tile
+  int R0, R1;              // rows of the query tile
+  int64_t lo, hi;          // clip window in keys of the visiting order
+  int64_t total;           // keys of the spans flushed so far
+  bool has;
+  Span cur;
 
+  __device__ void init(Span* o, int c, int r0, int r1, int64_t l, int64_t h) {
+    out = o; n = 0; cap = c; R0 = r0; R1 = r1; lo = l; hi = h; total = 0; has = false;
+  }
+  __device__ void flush() {
+    if (!has) return;
+    has = false;
+    const int64_t len = cur.k1 - cur.k0;
+    const int64_t a = lo > total ? lo : total;
+    const int64_t b = hi < total + len ? hi : total + len;
+    if (out && a < b && n < cap) {
+      Span s = cur;
+      s.k0 = cur.k0 + (int)(a - total);
+      s.k1 = s.k0 + (int)(b - a);
+      out[n++] = s;
+    }
+    total += len;
+  }
   __device__ void emit(int src, int k0, int k1, int r0, int r1) {
     if (k1 <= k0) return;
     const int a = max(r0, R0), b = min(r1, R1);
     if (a >= b) return;  // no row of this tile sees it
     const int full = (r0 <= R0 && R1 <= r1) ? 1 : 0;
     if (full) { r0 = 0; r1 = INT_MAX; }
-    if (n > 0) {
-      Span& s = out[n - 1];
-      if (s.src == src && s.k1 == k0 && s.r0 == r0 && s.r1 == r1) {
-        s.k1 = k1;
-        return;
-      }
+    if (has && cur.src == src && cur.k1 == k0 && cur.r0 == r0 && cur.r1 == r1) {
+      cur.k1 = k1;
+      return;
     }
-    if (n < cap) {
-      Span s;
-      s.src = src; s.k0 = k0; s.k1 = k1; s.r0 = r0; s.r1 = r1; s.full = full;
-      s.pad0 = 0; s.pad1 = 0;
-      out[n++] = s;
-    }
+    flush();
+    cur.src = src; cur.k0 = k0; cur.k1 = k1; cur.r0 = r0; cur.r1 = r1; cur.full = full;
+    cur.pad0 = 0; cur.pad1 = 0;
+    has = true;
+  }
+  __device__ int finish() {
+    flush();
+    return n;
   }
 };
 
@@ -82,13 +108,7 @@ __device__ void emit_ring_tile(SpanWriter& w, const PlanParams& p, int c) {
 }
 
 // Spans of text-query tile tt (text rows [tt*tile_q, ...)).
-__device__ int build_text_spans(const PlanParams& p, int tt, Span* out) {
-  SpanWriter w;
-  w.out = out;
-  w.n = 0;
-  w.cap = p.max_spans;
-  w.R0 = tt * p.tile_q;
-  w.R1 = min(w.R0 + p.tile_q, p.text_len);
+__device__ void emit_text_spans(const PlanParams& p, SpanWriter& w) {
   w.emit(SRC_HEADS, 0, p.head_tokens, 0, INT_MAX);
   w.emit(SRC_RING, 0, p.ring_tokens, 0, INT_MAX);
   w.emit(SRC_TXT, 0, p.head_len, 0, INT_MAX);
@@ -97,19 +117,10 @@ __device__ int build_text_spans(const PlanParams& p, int tt, Span* out) {
     w.emit(SRC_TXT, off, off + p.tail_len[j], off, off + p.tail_len[j]);
   }
   w.emit(SRC_VID, 0, p.lq, 0, INT_MAX);
-  return w.n;
 }
 
-// Full span list of query tile qt (video tiles, then text tiles).
-__device__ int build_tile_spans(const PlanParams& p, int qt, Span* out) {
-  if (qt >= p.n_qtiles) return build_text_spans(p, qt - p.n_qtiles, out);
-  SpanWriter w;
-  w.out = out;
-  w.n = 0;
-  w.cap = p.max_spans;
-  w.R0 = qt * p.tile_q;
-  w.R1 = min(w.R0 + p.tile_q, p.lq);
-
+// Spans of video query tile qt.
+__device__ void emit_video_spans(const PlanParams& p, int qt, SpanWriter& w) {
   int c_begin = 0, c_end = 0;
   if (p.sparse) {
     c_begin = p.row_ptr[qt];
@@ -153,7 +164,26 @@ __device__ int build_tile_spans(const PlanParams& p, int qt, Span* out) {
       }
     }
   }
-  return w.n;
+}
+
+// Spans of query tile qt (video tiles, then text tiles), clipped to the keys
+// [lo, hi) of its visiting order; returns the number written.  total_out, if
+// given, receives the tile's key count.
+__device__ int build_tile_spans(const PlanParams& p, int qt, Span* out, int64_t lo = 0,
+                                int64_t hi = INT64_MAX, int64_t* total_out = nullptr) {
+  SpanWriter w;
+  if (qt >= p.n_qtiles) {
+    const int r0 = (qt - p.n_qtiles) * p.tile_q;
+    w.init(out, p.max_spans, r0, min(r0 + p.tile_q, p.text_len), lo, hi);
+    emit_text_spans(p, w);
+  } else {
+    const int r0 = qt * p.tile_q;
+    w.init(out, p.max_spans, r0, min(r0 + p.tile_q, p.lq), lo, hi);
+    emit_video_spans(p, qt, w);
+  }
+  const int n = w.finish();
+  if (total_out) *total_out = w.total;
+  return n;
 }
 
 // Key position where split i of n begins (multiples of 64 keys).
@@ -162,32 +192,16 @@ __device__ int64_t split_bound(int64_t total, int i, int n) {
   return (total * i / n) & ~(int64_t)63;
 }
 
-// Span list of virtual tile vt = (query tile, key split).
+// Span list of virtual tile vt = (query tile, key split): a counting pass for
+// the tile's keys, then the spans clipped to this split's range.
 __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
   int qt, split, n_split;
   vt_decode(vt, p.n_qtiles, p.n_splits, p.n_splits_text, qt, split, n_split);
-  const int n = build_tile_spans(p, qt, out);
-  if (n_split == 1) return n;
+  if (n_split == 1) return build_tile_spans(p, qt, out);
   int64_t total = 0;
-  for (int i = 0; i < n; ++i) total += out[i].k1 - out[i].k0;
-  const int64_t a = split_bound(total, split, n_split);
-  const int64_t b = split_bound(total, split + 1, n_split);
-  // clip in place (entry m <= i is written only after entry i was read)
-  int m = 0;
-  int64_t pos = 0;
-  for (int i = 0; i < n; ++i) {
-    Span sp = out[i];
-    const int64_t len = sp.k1 - sp.k0;
-    const int64_t lo = a > pos ? a : pos;
-    const int64_t hi = b < pos + len ? b : pos + len;
-    if (lo < hi) {
-      sp.k0 += (int)(lo - pos);
-      sp.k1 = sp.k0 + (int)(hi - lo);
-      out[m++] = sp;
-    }
-    pos += len;
-  }
-  return m;
+  build_tile_spans(p, qt, nullptr, 0, INT64_MAX, &total);
+  return build_tile_spans(p, qt, out, split_bound(total, split, n_split),
+                          split_bound(total, split + 1, n_split));
 }
 
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
