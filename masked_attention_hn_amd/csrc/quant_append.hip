@@ -8,7 +8,7 @@
 //   q     = round_half_even(x / scale) (correctly rounded fp32 quotient),
 //           clamped to [-127, 127]; a zero row stores scale 0 and q 0.
 //
-// The kernel is HBM-bound streaming: 8 lanes own one row (16 bf16 = 32 bytes
+// The kernel streams rows: 8 lanes own one row (16 bf16 = 32 bytes
 // of K and 32 of V per lane), the row max is an 8-lane butterfly, and each
 // lane writes 16 int8 codes (one 16-byte store) per tensor.  Consecutive
 // 8-lane groups take the heads of one token, so each wave reads 8 x 256
@@ -21,9 +21,10 @@
 // from the correctly rounded quotient), and for zero, tiny, huge or
 // non-finite scales, does a group of 8 values take the compiler's correctly
 // rounded fp32 divide (no fast-math).  This cut the VALU work about 3x: +10%
-// on the 1280x704 segment's append, +4% on the six-segment history, no
-// change on the 480x832 segment, whose short launch is latency-bound.  fp32
-// denormals are preserved so subnormal scales quantize exactly.
+// on a 1280x704 segment's append with an 18-frame window (206 MB), +4% with
+// no window (337 MB), no change on the 480x832 segment (155 MB), whose short
+// launch is latency-bound.  fp32 denormals are preserved so subnormal scales
+// quantize exactly.
 #include "hn_internal.h"
 
 namespace hn {
