@@ -204,8 +204,16 @@ __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
                           split_bound(total, split + 1, n_split));
 }
 
+// One thread per virtual tile.  Text tiles start at a fresh wave, so that no
+// wave walks both the video and the text span builder one after the other.
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
-  const int vt = blockIdx.x * 64 + threadIdx.x;
+  const int i = blockIdx.x * 64 + threadIdx.x;
+  const int n_vid = p.n_qtiles * p.n_splits;
+  const int pad = (n_vid + 63) & ~63;
+  int vt;
+  if (i < n_vid) vt = i;
+  else if (i < pad) return;
+  else vt = n_vid + (i - pad);
   if (vt >= vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text)) return;
   counts[vt] = build_spans(p, vt, spans + (int64_t)vt * p.max_spans);
 }
@@ -257,7 +265,10 @@ hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
   const int n_vt = vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text);
   Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(n_vt));
-  const int blocks = (n_vt + 63) / 64;
+  const int n_vid = p.n_qtiles * p.n_splits;
+  const int threads = ((n_vid + 63) & ~63) + (n_vt - n_vid);
+  const int blocks = (threads + 63) / 64;
+  if (blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(plan_kernel, dim3(blocks), dim3(64), 0, s, p, counts, spans);
   return hipGetLastError();
 }
