@@ -11,6 +11,9 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <queue>
+#include <vector>
+
 #include "hn_internal.h"
 
 namespace {
@@ -126,18 +129,53 @@ int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu)
   return 1;
 }
 
-// Key splits per text query tile.  The text tiles of a joint launch come
-// after all video tiles and add a fraction of a round of blocks (the 480x832
-// segment: 80 text tasks after 736 video tasks on 256 CUs); in quarters they
-// fill the last round instead of adding one.  Text tiles with fewer than
-// 4096 keys are not split.  HN_ATTN_TEXT_SPLITS=n forces n.
-int choose_text_splits(int64_t text_tiles, int64_t keys_per_tile) {
+// Key splits per text query tile.  The text tiles of a joint launch run after
+// the video tiles and fill what the video blocks leave of the last round, or
+// rounds of their own.  The count taken is the one whose estimated makespan is
+// least when the blocks are dealt in order to the earliest free slot (the
+// video blocks first, all of one size, then the text pieces), each block
+// costing its keys plus a fixed 1,600 key-equivalents (Q load, first tile,
+// partial write, share of the merge), a constant fitted to same-run
+// measurements: 4 splits on the 480x832 segment, where the video leaves 32 of
+// 256 slots free in its last round, and 8 on the 1280x704 one, where it fills
+// its last round (joint launch 2.5% faster than with 4).  Text tiles with
+// fewer than 4096 keys are not split, and pieces keep at least 1,024 keys.
+// HN_ATTN_TEXT_SPLITS=n forces n.
+int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, int n_text_tiles,
+                       int64_t keys_per_tile, int blocks_per_cu) {
   if (const char* e = std::getenv("HN_ATTN_TEXT_SPLITS")) {
     const int v = std::atoi(e);
     if (v >= 1 && v <= HN_MAX_SPLITS) return v;
   }
-  if (text_tiles <= 0 || keys_per_tile < 4096) return 1;
-  return 4;
+  if (n_text_tiles <= 0 || keys_per_tile < 4096) return 1;
+  constexpr double kOverhead = 1600.0;
+  const int64_t slots = std::max<int64_t>(device_cus() * std::max(blocks_per_cu, 1), 1);
+  const int64_t q = video_tasks / slots, r = video_tasks % slots;
+  const double kv = (double)video_keys_per_task + kOverhead;
+  int best = 1;
+  double best_t = 0.0;
+  for (int sp = 1; sp <= HN_MAX_SPLITS; sp *= 2) {
+    if (sp > 1 && keys_per_tile / sp < 1024) break;
+    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+    for (int64_t i = 0; i < slots; ++i) free_at.push((double)(q + (i < r ? 1 : 0)) * kv);
+    const double kt = (double)keys_per_tile / sp + kOverhead;
+    const int64_t pieces = (int64_t)H * n_text_tiles * sp;
+    for (int64_t i = 0; i < pieces; ++i) {
+      const double t = free_at.top();
+      free_at.pop();
+      free_at.push(t + kt);
+    }
+    double t_end = 0.0;
+    while (!free_at.empty()) {
+      t_end = std::max(t_end, free_at.top());
+      free_at.pop();
+    }
+    if (sp == 1 || t_end < best_t * (1.0 - 1e-9)) {
+      best_t = t_end;
+      best = sp;
+    }
+  }
+  return best;
 }
 
 // Query rows per tile of a plan: keep lists fix HN_TILE; dense plans use the
@@ -196,7 +234,10 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     // dense 256-row blocks run one per CU, 128-row blocks two
     pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video, pp->tile_q >= 256 ? 1 : 2);
     // text queries see heads, the whole ring and the own video (no keep list)
-    pp->n_splits_text = choose_text_splits(pp->n_text_tiles, keys + (int64_t)pp->ring_tokens + lq);
+    const int bpc = pp->tile_q >= 256 ? 1 : 2;
+    pp->n_splits_text = choose_text_splits(c->num_heads, (int64_t)c->num_heads * pp->n_qtiles * pp->n_splits,
+                                           (keys + video) / pp->n_splits, pp->n_text_tiles,
+                                           keys + (int64_t)pp->ring_tokens + lq, bpc);
   }
   int max_spans = 4 + s->num_actions;
   if (sp) {

@@ -251,6 +251,34 @@ def test_automatic_two_splits_fill_the_last_round(monkeypatch):
     assert ws(*share) == ws(*share, splits=1)
 
 
+def test_text_split_count_follows_the_round_model(monkeypatch):
+    """Without a device (256 compute units assumed): the text tiles of a joint
+    launch are split so that they fill what the video blocks leave free.  The
+    480x832 segment (736 unsplit video blocks: 32 slots free in the last
+    round) takes 4; the 1280x704 steady state (video split in two: 13 full
+    rounds) takes 8; short text tiles stay whole.  The automatic workspace
+    size must equal the one of the forced count."""
+    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
+
+    def ws(H, P, frames, W_, text_splits=None, head=768, tails=(128,) * 4):
+        if text_splits is None:
+            monkeypatch.delenv("HN_ATTN_TEXT_SPLITS", raising=False)
+        else:
+            monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", str(text_splits))
+        c = fake_cache(H=H, P=P, W=W_, cap=4096)
+        c.frames_seen = W_ if W_ > 1 else 0   # a full ring of history (none for the first segment)
+        c.segments = 0
+        seg = hn.SegLayout(0, frames, P, head, list(tails), [0] * len(tails), [frames] * len(tails))
+        return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+
+    first = (16, 390, 30, 1)
+    assert ws(*first) == ws(*first, text_splits=4) != ws(*first, text_splits=8)
+    steady = (16, 880, 30, 18)
+    assert ws(*steady) == ws(*steady, text_splits=8) != ws(*steady, text_splits=4)
+    short = (2, 24, 2, 4)
+    assert ws(*short, head=16, tails=(8, 8)) == ws(*short, text_splits=1, head=16, tails=(8, 8))
+
+
 def test_archive_checks():
     """Validation of hn_kv_archive_evict / hn_kv_cache_rewind on the host
     (cases that copy nothing; the copies themselves are GPU tests)."""
