@@ -138,7 +138,9 @@ int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu)
 // partial write, share of the merge), a constant fitted to same-run
 // measurements: 4 splits on the 480x832 segment, where the video leaves 32 of
 // 256 slots free in its last round, and 8 on the 1280x704 one, where it fills
-// its last round (joint launch 2.5% faster than with 4).  Text tiles with
+// its last round (joint launch 2.5% faster than with 4); ties go to the fewer
+// splits (the 2-head share's 10 text tiles run whole beside its 208 video
+// blocks).  Text tiles with
 // fewer than 4096 keys are not split, and pieces keep at least 1,024 keys.
 // HN_ATTN_TEXT_SPLITS=n forces n.
 int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, int n_text_tiles,
