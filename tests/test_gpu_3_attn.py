@@ -92,7 +92,13 @@ def test_deterministic_bitwise():
     run = G.Run(w, d)
     o1, l1 = run.attn()
     o2, l2 = run.attn()
-    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    a, b = o1.view(torch.int16), o2.view(torch.int16)
+    if not torch.equal(a, b):
+        diff = (a != b).nonzero().cpu().numpy()        # [row, head, d]
+        rows, heads = np.unique(diff[:, 0]), np.unique(diff[:, 1])
+        mag = (o1.float() - o2.float()).abs().max().item()
+        raise AssertionError(f"{len(diff)} elements differ: rows {rows[:16]}... ({len(rows)}), "
+                             f"heads {heads}, max |diff| {mag}")
     assert torch.equal(l1, l2)
 
 
