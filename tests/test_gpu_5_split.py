@@ -89,3 +89,18 @@ def test_head_share_forced_split():
     err = _bar(w, o.float().cpu().numpy()[rows], ref)
     print(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
     assert np.abs(lse.cpu().numpy()[:, rows] - ref_lse).max() <= 1e-2
+
+
+def test_split_joint_deterministic_bitwise(monkeypatch):
+    """A joint launch with video and text tiles split (partials merged) gives
+    bit-identical outputs on repeated calls with the same plan."""
+    monkeypatch.setenv("HN_ATTN_SPLITS", "4")
+    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "3")
+    w = W.config("m1")
+    run = G.Run(w, data_of("m1"))
+    first = [t.clone() for t in run.attn_joint()]
+    for _ in range(3):
+        for a, b in zip(run.attn_joint(), first):
+            if a.dtype == torch.bfloat16:
+                a, b = a.view(torch.int16), b.view(torch.int16)
+            assert torch.equal(a, b)
