@@ -245,16 +245,19 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
  * the video queries, tiles n_qtiles .. n_qtiles+n_text_tiles-1 the text
  * queries (head and tails).
  * Split-KV: when (heads x video query tiles) would leave the GPU's block
- * slots (2 per compute unit) poorly filled, every query tile's keys are
- * split into n_splits contiguous ranges that run as separate blocks; each
- * writes a partial result into the workspace and a merge kernel combines
- * them (one softmax, exactly as without the split up to rounding).  The
- * split count comes from the device's compute-unit count and the layout;
- * HN_ATTN_SPLITS=n in the environment forces n (1..16).  Text query tiles,
- * which follow all video tiles in a joint launch, are split 4 ways when they
- * visit at least 4096 keys, so that they fill the launch's last round of
- * blocks (HN_ATTN_TEXT_SPLITS=n forces n).  Dense plans use
- * 256-row query tiles (HN_ATTN_DENSE_ROWS=128 forces 128-row ones).  With n_splits > 1
+ * slots (one per compute unit for 256-row tiles, two for 128-row ones)
+ * poorly filled, every query tile's keys are split into n_splits contiguous
+ * ranges that run as separate blocks; each writes a partial result into the
+ * workspace and a merge kernel combines them (one softmax, exactly as
+ * without the split up to rounding).  The split count comes from the
+ * device's compute-unit count and the layout; HN_ATTN_SPLITS=n in the
+ * environment forces n (1..16).  Text query tiles, which follow all video
+ * tiles in a joint launch, get their own count: the one (of 1, 2, 4, 8, 16)
+ * with the least estimated makespan when the blocks are dealt to the slots
+ * in order, so that they fill what the video blocks leave free; tiles of
+ * fewer than 4096 keys stay whole (HN_ATTN_TEXT_SPLITS=n forces n).  Dense
+ * plans use 256-row query tiles (HN_ATTN_DENSE_ROWS=128 forces 128-row
+ * ones).  With n_splits > 1
  * attention calls that share one plan workspace must not overlap in time
  * (same stream, or ordered), since they write its partial area. */
 typedef struct hn_tile_plan {
