@@ -86,9 +86,13 @@ def test_attention_full_size_sampled_rows(name):
         _DATA.pop(name)
 
 
-def test_deterministic_bitwise():
-    w = W.config("m2")
-    d = data_of("m2")
+@pytest.mark.parametrize("name", ["m2", "m4", "c2", "c5"])
+def test_deterministic_bitwise(name):
+    # dense plans (256-row blocks): m2, and c2 at full size (every CU busy);
+    # keep-list plans (128-row blocks): m4, and c5 at full size
+    print(f"[attn] bitwise repeat {name}", flush=True)
+    w = W.config(name)
+    d = data_of(name)
     run = G.Run(w, d)
     o1, l1 = run.attn()
     o2, l2 = run.attn()
