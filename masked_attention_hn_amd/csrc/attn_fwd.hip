@@ -623,12 +623,11 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
 // softmax over the union of their keys: with M = max_s lse_s and
 // w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s and
 // lse = M + log(sum_s w_s); rows no split saw (all lse = -inf) get O = 0.
-// Block = one (head, tile); lane group of 32 covers one 128-wide row with
-// float4 loads, 8 rows in flight per pass.
-// One block per 32 rows of a (head, query tile): with one block per whole
-// tile, a launch that merges only a few split tiles (the text tiles of a
-// joint launch: 80 blocks) was bound by 32 dependent load round trips per
-// block, 82-89 us on the 480x832 segment.
+// Block = MERGE_ROWS rows of one (head, query tile); each 32-lane group
+// merges one 128-wide row with float4 loads.  With one block per whole tile,
+// a launch that merges only a few split tiles (the text tiles of a joint
+// launch: 80 blocks) was bound by 32 dependent load round trips per block,
+// 82-89 us on the 480x832 segment.
 constexpr int MERGE_ROWS = 8;
 __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int chunks = (p.tile_rows + MERGE_ROWS - 1) / MERGE_ROWS;

@@ -182,8 +182,9 @@ int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, 
 
 // Query rows per tile of a plan: keep lists fix HN_TILE; dense plans use the
 // kernel's 256-row blocks (faster than 128-row ones even where 256-row blocks
-// leave compute units idle: the 2-head share above runs 1.386 ms with 208
-// such blocks, 1.545 ms with 414 128-row blocks).
+// leave compute units idle: in one run the 2-head share above took
+// 1.215-1.217 ms with 208 such blocks against 1.464 ms with 414 128-row
+// blocks, and 1.45-1.47 against 1.67-1.68 ms with its text queries).
 // HN_ATTN_DENSE_ROWS=128|256 in the environment forces the height (tuning, tests).
 int plan_tile_rows(bool sparse) {
   if (sparse) return HN_TILE;

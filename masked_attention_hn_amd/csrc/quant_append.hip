@@ -36,7 +36,8 @@ namespace {
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// Quantize the 8 values this lane holds; amax is the row maximum.
+// Codes of the 8 values this lane holds, by the correctly rounded quotient
+// x / scale; zero marks an all-zero row (codes 0).
 __device__ inline uint2 quant8(const float (&x)[8], float scale, bool zero) {
   uint32_t b[8];
 #pragma unroll
