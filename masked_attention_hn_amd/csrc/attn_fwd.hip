@@ -22,9 +22,16 @@
 //            per-lane offsets are fixed for the block, each tile adds a scalar
 //            offset, and the buffer bound returns 0 past a source's end.
 //            INT8 tiles are read from HBM as int8 (half the bytes) with their
-//            per-token fp32 scales and dequantized to bf16 (code x scale,
-//            correctly rounded in fp32, then rounded to bf16) in registers on
-//            their way into LDS, so the math never sees a scale.
+//            per-token fp32 scales and dequantized in registers on their way
+//            into LDS, so the math never sees a scale.  They are staged and
+//            multiplied in fp16, not bf16: K' = fp16(code x scale) and
+//            V' = fp16(code x scale x 2^-7), against an fp16 copy of Q and
+//            fp16 probabilities that carry the 2^7 back.  fp16 keeps 11
+//            significant bits where bf16 keeps 8, which bounds the error of the
+//            dequantized history 8x tighter at the same MFMA rate; the
+//            power-of-two shifts keep K', V' and P inside fp16's range.  A tile
+//            whose scales would leave that range (|K| above 65,024 or |V| above
+//            8.3e6) falls back to bf16 K and V.
 //   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then holds
 //            the tile's keys for one query, so the row max/sum are in-lane plus
 //            one v_permlane32_swap with lane^32); online softmax in the log2
@@ -45,6 +52,7 @@
 //            contiguous range of (head, tile) tasks, so one head's keys and
 //            values stay in one XCD's L2.
 #include <climits>
+#include <type_traits>
 
 #include "hn_internal.h"
 
@@ -54,9 +62,18 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag
+// fp16 staging of INT8 tiles.  Probabilities are <= 2^RESCALE_SLACK, so with
+// the 2^7 shift they stay <= 2^15; codes are <= 127 in magnitude, so
+// K' = code x ks fits fp16 (max 65504) for ks <= 512 and V' = code x vs x 2^-7
+// for vs <= 65536.
+constexpr float P_SHIFT = 7.0f;
+constexpr float KS_MAX_F16 = 512.0f;
+constexpr float VS_MAX_F16 = 65536.0f;
 template <int NW_, int QB_, int KT_>
 struct Cfg {
   static constexpr int NW = NW_, QB = QB_, KT = KT_;
@@ -94,6 +111,9 @@ struct Stage {
 
 struct TileDesc {
   int src, kb, nk, r0, r1;
+  // INT8 tile staged in fp16 whose scales fit fp16's range (set when the
+  // tile is stored)
+  bool ok16;
 };
 
 // max / sum of a value and its lane^32 partner
@@ -121,27 +141,37 @@ __device__ inline void ld_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t sof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
-// Four INT8 codes of w times the row scale sc -> two packed bf16 pairs.
-// With u = q + 128 (the codes' bytes xor 0x80), fma(u, sc, -128 sc) is the
-// correctly rounded fp32 product q * sc (128 sc is exact), then rounded to bf16.
+// Four INT8 codes of w times the row scale sc -> two packed fp16 (F16) or
+// bf16 pairs.  With u = q + 128 (the codes' bytes xor 0x80), fma(u, sc,
+// -128 sc) is the correctly rounded fp32 product q * sc (128 sc is exact),
+// then rounded to the 16-bit type.
+template <bool F16>
 __device__ inline void i8x4_dequant(uint32_t w, float sc, float m128, uint32_t& p0, uint32_t& p1) {
   const uint32_t u = w ^ 0x80808080u;
   const float f0 = __builtin_fmaf((float)(u & 0xffu), sc, m128);
   const float f1 = __builtin_fmaf((float)((u >> 8) & 0xffu), sc, m128);
   const float f2 = __builtin_fmaf((float)((u >> 16) & 0xffu), sc, m128);
   const float f3 = __builtin_fmaf((float)(u >> 24), sc, m128);
-  const bf16x2 a = {(__bf16)f0, (__bf16)f1};
-  const bf16x2 b = {(__bf16)f2, (__bf16)f3};
-  p0 = __builtin_bit_cast(uint32_t, a);
-  p1 = __builtin_bit_cast(uint32_t, b);
+  if constexpr (F16) {
+    const f16x2 a = {(_Float16)f0, (_Float16)f1};
+    const f16x2 b = {(_Float16)f2, (_Float16)f3};
+    p0 = __builtin_bit_cast(uint32_t, a);
+    p1 = __builtin_bit_cast(uint32_t, b);
+  } else {
+    const bf16x2 a = {(__bf16)f0, (__bf16)f1};
+    const bf16x2 b = {(__bf16)f2, (__bf16)f3};
+    p0 = __builtin_bit_cast(uint32_t, a);
+    p1 = __builtin_bit_cast(uint32_t, b);
+  }
 }
-// 16 INT8 codes of one row -> 16 dequantized bf16 (two 16-byte words).
+// 16 INT8 codes of one row -> 16 dequantized 16-bit values (two 16-byte words).
+template <bool F16>
 __device__ inline void i8x16_dequant(uint4 w, float sc, uint4& lo, uint4& hi) {
   const float m128 = -128.0f * sc;
-  i8x4_dequant(w.x, sc, m128, lo.x, lo.y);
-  i8x4_dequant(w.y, sc, m128, lo.z, lo.w);
-  i8x4_dequant(w.z, sc, m128, hi.x, hi.y);
-  i8x4_dequant(w.w, sc, m128, hi.z, hi.w);
+  i8x4_dequant<F16>(w.x, sc, m128, lo.x, lo.y);
+  i8x4_dequant<F16>(w.y, sc, m128, lo.z, lo.w);
+  i8x4_dequant<F16>(w.z, sc, m128, hi.x, hi.y);
+  i8x4_dequant<F16>(w.w, sc, m128, hi.z, hi.w);
 }
 
 template <class C>
@@ -235,27 +265,25 @@ __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rk
 }
 
 // INT8 tile: convert and write the operand-major layouts (row r = 64 rg + lane,
-// codes [16 dch, 16 dch + 16)).
-template <class C>
-__device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
+// codes [16 dch, 16 dch + 16)), in fp16 (F16) or bf16.
+template <class C, bool F16>
+__device__ inline void store_i8_as(Stage<C>& sb, const Prefetch<C>& pf, float ks, float vs) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int r = (tid & 63) + 64 * (wave % C::RG);
   const int kb32 = r >> 5, q32 = r & 31;
   // V slot coordinates of row r
   const int h = (r >> 4) & 1, half = (r >> 3) & 1, g = (r >> 2) & 1, qq = r & 3;
-  // rows past the tile's valid keys become zeros
-  const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
 #pragma unroll
   for (int c8 = 0; c8 < C::CH8; ++c8) {
     const int dch = c8 * (C::NW / C::RG) + wave / C::RG;
     uint4 lo, hi;
-    i8x16_dequant(pf.k[c8], ks, lo, hi);
+    i8x16_dequant<F16>(pf.k[c8], ks, lo, hi);
     // d chunks 2dch (g=0) and 2dch+1 (g=1) of K block (kb32, t = dch)
     __bf16* kblk = &sb.k[(kb32 * 8 + dch) * 512];
     *reinterpret_cast<uint4*>(kblk + q32 * 8) = lo;
     *reinterpret_cast<uint4*>(kblk + (32 + q32) * 8) = hi;
-    i8x16_dequant(pf.v[c8], vs, lo, hi);
+    i8x16_dequant<F16>(pf.v[c8], vs, lo, hi);
     // columns 16 dch .. +16 -> c = dch / 2, G&1 = dch % 2, slots 16G + 4qq + {0..3}
     const int c = dch >> 1, G = 2 * g + (dch & 1);
     __bf16* vblk = &sb.v[(((c * C::KB + kb32) * 2 + h) * 2 + half) * 256];
@@ -263,25 +291,41 @@ __device__ inline void store_i8(Stage<C>& sb, const Prefetch<C>& pf) {
     *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4 + 8) = hi;
   }
 }
+// Stages an INT8 tile: in fp16 (F16: K' = code x ks, V' = code x vs x
+// 2^-P_SHIFT; t.ok16 says whether every scale of the tile fits fp16's range,
+// which every wave decides alike since each holds the scales of all the
+// tile's rows), or in bf16 (code x scale rounded to bf16).
+template <class C, bool F16>
+__device__ inline void store_i8(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf) {
+  static_assert(C::RG == 1, "the staging decision needs every row's scale in every wave");
+  // rows past the tile's valid keys become zeros
+  const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
+  if constexpr (F16) {
+    t.ok16 = !__any(!(ks <= KS_MAX_F16 && vs <= VS_MAX_F16));
+    store_i8_as<C, true>(sb, pf, ks, vs * 0x1p-7f);
+  } else {
+    store_i8_as<C, false>(sb, pf, ks, vs);
+  }
+}
 
-// Start loading tile t into LDS buffer b: bf16 tiles land in LDS directly
-// (their unit scales are written here); INT8 tiles go to registers and are
-// stored by finish_tile.
-template <class C>
+// Start loading tile t into LDS buffer b: bf16 tiles land in LDS directly;
+// INT8 tiles go to registers and are stored by finish_tile (I8: 0 = no INT8
+// tiles, 1 = staged in fp16, 2 = staged in bf16).
+template <class C, int I8>
 __device__ inline void start_tile(const Sources& S, const TileDesc& t, Stage<C>& sb, Prefetch<C>& pf) {
-  const int tid = threadIdx.x;
   if (t.src >= SRC_TXT) {
     if (t.src == SRC_VID) load_bf16<C>(S, S.k_vid, S.v_vid, t.kb, sb);
     else load_bf16<C>(S, S.k_txt, S.v_txt, t.kb, sb);
-  } else if (t.src == SRC_RING) {
-    load_i8<C>(S, S.k_ring, S.v_ring, S.ks_ring, S.vs_ring, t.kb, t.nk, pf);
-  } else {
-    load_i8<C>(S, S.k_heads, S.v_heads, S.ks_heads, S.vs_heads, t.kb, t.nk, pf);
+  } else if constexpr (I8 != 0) {
+    if (t.src == SRC_RING) load_i8<C>(S, S.k_ring, S.v_ring, S.ks_ring, S.vs_ring, t.kb, t.nk, pf);
+    else load_i8<C>(S, S.k_heads, S.v_heads, S.ks_heads, S.vs_heads, t.kb, t.nk, pf);
   }
 }
-template <class C>
-__device__ inline void finish_tile(const TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf) {
-  if (t.src < SRC_TXT) store_i8<C>(sb, pf);
+template <class C, int I8>
+__device__ inline void finish_tile(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf) {
+  if constexpr (I8 != 0) {
+    if (t.src < SRC_TXT) store_i8<C, I8 == 1>(t, sb, pf);
+  }
 }
 
 __device__ inline bf16x8 ld8(const __bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
@@ -299,11 +343,21 @@ __device__ inline bf16x8 tr_read8(const __bf16* p0, const __bf16* p1) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
+// Eight probabilities as the B operand of the PV MFMA: bf16, or fp16 bits
+// for the fp16 path (same register layout).
+template <bool F16>
 __device__ inline bf16x8 pack_p(const float* x) {
-  bf16x8 r;
+  if constexpr (F16) {
+    f16x8 r;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
-  return r;
+    for (int j = 0; j < 8; ++j) r[j] = (_Float16)x[j];
+    return __builtin_bit_cast(bf16x8, r);
+  } else {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (__bf16)x[j];
+    return r;
+  }
 }
 
 struct RowState {
@@ -313,14 +367,18 @@ struct RowState {
 
 // One KT-key tile for one wave: S^T = K Q^T, online softmax, O^T += V^T P^T.
 //   MASK : some keys (ragged end) or rows (tail window) of the tile are invisible
+//   QK16 : INT8 tile: K' is fp16 and qreg holds the fp16 copy of Q
+//   PV16 : V' is fp16 carrying 2^-P_SHIFT; the probabilities are taken as
+//          p * 2^P_SHIFT in fp16 (else both are bf16)
 // The QK MFMAs of the whole tile are issued first, then one rescale decision
 // is taken from the maxima of all its 32-key blocks, so that the exponentials
 // and PV MFMAs of the blocks form one straight-line region.  The row sum adds
-// the bf16 probabilities the PV MFMA consumes.
-template <class C, bool MASK>
+// the 16-bit probabilities the PV MFMA consumes, so their rounding cancels in
+// O = acc / l.  scale[q] is the score scale (log2 units) of query block q.
+template <class C, bool MASK, bool QK16, bool PV16>
 __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8],
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
-                                          float scale_log2, int nk, const bool (&row_ok)[C::QB]) {
+                                          const float (&scale)[C::QB], int nk, const bool (&row_ok)[C::QB]) {
   constexpr int QB = C::QB, KB = C::KB;
   const int lane = threadIdx.x & 63;
   const int g = lane >> 5, l32 = lane & 31;
@@ -346,8 +404,13 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
     for (int i = 0; i < NK; ++i) {
       const int t = i / KB, kb = i % KB;
 #pragma unroll
-      for (int q = 0; q < QB; ++q)
-        s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[i], qreg[q][t], s[q][kb], 0, 0, 0);
+      for (int q = 0; q < QB; ++q) {
+        if constexpr (QK16)
+          s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kk[i]),
+                                                            __builtin_bit_cast(f16x8, qreg[q][t]), s[q][kb], 0, 0, 0);
+        else
+          s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[i], qreg[q][t], s[q][kb], 0, 0, 0);
+      }
       if (i + KLOOK < NK) kk[i + KLOOK] = ld8(kl + (((i + KLOOK) % KB) * 8 + (i + KLOOK) / KB) * 512);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -366,7 +429,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            float v = s[q][kb][4 * r + i] * scale_log2;
+            float v = s[q][kb][4 * r + i] * scale[q];
             if (kb * 32 + 8 * r + i >= nkg) v = -INFINITY;
             s[q][kb][4 * r + i] = v;
             mx = fmaxf(mx, v);
@@ -375,7 +438,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
         float m0 = s[q][kb][0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) m0 = fmaxf(m0, s[q][kb][i]);
-        mx = fmaxf(mx, m0 * scale_log2);
+        mx = fmaxf(mx, m0 * scale[q]);
       }
     }
     mx = pair_max(mx);
@@ -388,13 +451,14 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
       for (int c = 0; c < 4; ++c) acc[q][c] *= alpha;
     }
     m_use[q] = (st[q].m == -INFINITY) ? 0.0f : st[q].m;
+    if constexpr (PV16) m_use[q] -= P_SHIFT;  // probabilities times 2^P_SHIFT
   }
 
   // probabilities of block kb, element i, in place of its scores (on the
   // masked path the scores are already scaled, and -inf where invisible)
   auto prob = [&](int q, int kb, int i) __attribute__((always_inline)) {
     if (MASK) s[q][kb][i] = __builtin_amdgcn_exp2f(s[q][kb][i] - m_use[q]);
-    else s[q][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][i], scale_log2, -m_use[q]));
+    else s[q][kb][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[q][kb][i], scale[q], -m_use[q]));
   };
   bf16x8 pb[KB][QB][2];
   // slice j (0..7) of block kb's softmax: two exponentials per query block;
@@ -409,13 +473,24 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) pv[e] = s[q][kb][8 * h + e];
-        pb[kb][q][h] = pack_p(pv);
-        const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+        pb[kb][q][h] = pack_p<PV16>(pv);
         float l = st[q].l;
+        if constexpr (PV16) {
+          // sum of the fp16 probabilities, each times 2^-P_SHIFT (exact)
+          const f16x8 ph = __builtin_bit_cast(f16x8, pb[kb][q][h]);
+          const f16x2 unshift = {(_Float16)0x1p-7f, (_Float16)0x1p-7f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16x2 pp = {pb[kb][q][h][2 * e], pb[kb][q][h][2 * e + 1]};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
+          for (int e = 0; e < 4; ++e) {
+            const f16x2 pp = {ph[2 * e], ph[2 * e + 1]};
+            l = __builtin_amdgcn_fdot2(pp, unshift, l, false);
+          }
+        } else {
+          const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bf16x2 pp = {pb[kb][q][h][2 * e], pb[kb][q][h][2 * e + 1]};
+            l = __builtin_amdgcn_fdot2_f32_bf16(pp, one, l, false);
+          }
         }
         st[q].l = l;
       }
@@ -441,15 +516,29 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   for (int i = 0; i < NP; ++i) {
     const int kb = i / 8, t = (i / 4) % 2, c = i % 4;
 #pragma unroll
-    for (int q = 0; q < QB; ++q)
-      acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[i], pb[kb][q][t], acc[q][c], 0, 0, 0);
+    for (int q = 0; q < QB; ++q) {
+      if constexpr (PV16)
+        acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, vv[i]),
+                                                           __builtin_bit_cast(f16x8, pb[kb][q][t]),
+                                                           acc[q][c], 0, 0, 0);
+      else
+        acc[q][c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vv[i], pb[kb][q][t], acc[q][c], 0, 0, 0);
+    }
     if (i + VLOOK < NP) vv[i + VLOOK] = tr_read8(vaddr(i + VLOOK), vaddr(i + VLOOK) + 256);
     if (kb + 1 < KB) slice(kb + 1, i % 8);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <class C, int MIN_BLOCKS>
+// HAS_I8: the plan has INT8 history sources (description heads or ring
+// frames); without them the kernel carries no INT8 or fp16 code.
+//
+// Every span list visits its INT8 sources (earlier heads, ring frames) before
+// the bf16 ones of the current segment, so a block runs in two phases: the
+// INT8 tiles with the fp16 copy of Q in qreg, then the bf16 tiles with Q
+// reloaded as bf16 into the same registers.  One copy of Q is live at a time
+// (both do not fit two waves per SIMD beside the rest).
+template <class C, int MIN_BLOCKS, bool HAS_I8>
 __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnParams p) {
   constexpr int QB = C::QB;
   __shared__ Stage<C> stage0;
@@ -479,15 +568,16 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   // Q^T as the B operand: lane (q, g) holds Q[q][16t + 8g .. +8] for t = 0..7;
   // rows past the segment read as 0
   bf16x8 qreg[QB][8];
-  {
-    const uint32_t tb = (uint32_t)p.H * D * 2;
-    const rsrc_t rq = make_rsrc(qsrc + h * D, (uint32_t)lq * tb - (uint32_t)h * D * 2);
+  const uint32_t q_tb = (uint32_t)p.H * D * 2;
+  const rsrc_t rq = make_rsrc(qsrc + h * D, (uint32_t)lq * q_tb - (uint32_t)h * D * 2);
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < QB; ++q)
 #pragma unroll
       for (int t = 0; t < 8; ++t)
-        qreg[q][t] = __builtin_bit_cast(bf16x8, ld_b128(rq, (uint32_t)row[q] * tb + 16 * g, 32 * t));
-  }
+        qreg[q][t] = __builtin_bit_cast(bf16x8, ld_b128(rq, (uint32_t)row[q] * q_tb + 16 * g, 32 * t));
+  };
+  load_q();
   Sources S;
   init_sources<C>(p, h, S);
 
@@ -518,6 +608,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     t.nk = min(C::KT, sp.k1 - kpos);
     t.r0 = sp.r0;
     t.r1 = sp.r1;
+    t.ok16 = true;
     kpos += t.nk;
     if (kpos >= sp.k1) {
       ++e;
@@ -529,53 +620,131 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     return true;
   };
 
-  // One pipeline step: compute tile `cur` from stage `sc` while tile `nxt`
-  // streams into stage `sn`; the stages alternate, unrolled by two so that
-  // each step's stages are distinct objects.
   TileDesc cur, nxt;
   bool have = next_tile(cur);
-  if (have) {
-    Prefetch<C> pf;
-    start_tile<C>(S, cur, stage0, pf);
-    finish_tile<C>(cur, stage0, pf);
-  }
-  __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of this thread have landed
-  __syncthreads();
-  auto compute = [&](const Stage<C>& sc) __attribute__((always_inline)) {
-    // rows of this wave that see the tile; skip the math if none does
-    const int wrows = 32 * QB;
-    const bool wave_live = (cur.r0 < wrow0 + wrows) && (cur.r1 > wrow0);
-    if (wave_live) {
-      const bool rows_all = (cur.r0 <= wrow0) && (cur.r1 >= wrow0 + wrows);
-      bool row_ok[QB];
+  // Scores of the fp16 tiles: Q * 2^-qs per row, with qs = 0 unless the row
+  // holds a |Q| >= 2^15, then the least shift that brings it below 2^15 (a
+  // power of two: exact, and folded back into the score scale).
+  float scale_h[QB];
+  auto to_f16_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < QB; ++q) row_ok[q] = row[q] >= cur.r0 && row[q] < cur.r1;
-      const bool mask = (cur.nk < C::KT) || !rows_all;
-      const float sl = p.scale_log2;
-      // INT8 tiles sit in LDS already dequantized, so every source shares
-      // the two paths: full tiles and masked ones
-      if (mask) tile_math<C, true>(sc, qreg, acc, st, sl, cur.nk, row_ok);
-      else tile_math<C, false>(sc, qreg, acc, st, sl, cur.nk, row_ok);
+    for (int q = 0; q < QB; ++q) {
+      float mx = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) mx = fmaxf(mx, fabsf((float)qreg[q][t][i]));
+      mx = pair_max(mx);  // the row's other 64 values sit in lane ^ 32
+      const int qs = mx >= 0x1p15f ? ilogbf(mx) - 14 : 0;
+      const float f = ldexpf(1.0f, -qs);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        f16x8 x;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (_Float16)((float)qreg[q][t][i] * f);
+        qreg[q][t] = __builtin_bit_cast(bf16x8, x);
+      }
+      scale_h[q] = ldexpf(p.scale_log2, qs);
     }
   };
-  // The prefetch registers of an INT8 tile are fresh in every step (not
-  // carried around the loop), so no copies of them sit between the loads and
-  // the math of the current tile.
-  auto step = [&](const Stage<C>& sc, Stage<C>& sn) __attribute__((always_inline)) {
+  // the math of tile `cur` from stage sc: the rows of this wave that see it,
+  // full tiles on the lean path, ragged or row-cut ones on the masked path
+  auto compute = [&](const Stage<C>& sc, auto f16_tag) __attribute__((always_inline)) {
+    constexpr bool F16 = decltype(f16_tag)::value;
+    const int wrows = 32 * QB;
+    const bool wave_live = (cur.r0 < wrow0 + wrows) && (cur.r1 > wrow0);
+    if (!wave_live) return;
+    const bool rows_all = (cur.r0 <= wrow0) && (cur.r1 >= wrow0 + wrows);
+    bool row_ok[QB];
+    float sc_t[QB];
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      row_ok[q] = row[q] >= cur.r0 && row[q] < cur.r1;
+      sc_t[q] = F16 ? scale_h[q] : p.scale_log2;
+    }
+    const bool mask = (cur.nk < C::KT) || !rows_all;
+    if (mask) tile_math<C, true, F16, F16>(sc, qreg, acc, st, sc_t, cur.nk, row_ok);
+    else tile_math<C, false, F16, F16>(sc, qreg, acc, st, sc_t, cur.nk, row_ok);
+  };
+  // One pipeline step: compute tile `cur` from stage `sc` while tile `nxt`
+  // streams into stage `sn`; the stages alternate, unrolled by two so that
+  // each step's stages are distinct objects.  The prefetch registers of an
+  // INT8 tile are fresh in every step (not carried around the loop), so no
+  // copies of them sit between the loads and the math of the current tile.
+  // I8 = 1: the INT8 phase (fp16 math; the next tile may be INT8 or the first
+  // bf16 one); I8 = 2 / 0: bf16 math, INT8 tiles (if any) staged in bf16.
+  auto step = [&](const Stage<C>& sc, Stage<C>& sn, auto i8_tag) __attribute__((always_inline)) {
+    constexpr int I8 = decltype(i8_tag)::value;
     const bool have_next = next_tile(nxt);
     Prefetch<C> pf;
-    if (have_next) start_tile<C>(S, nxt, sn, pf);
-    compute(sc);
-    if (have_next) finish_tile<C>(nxt, sn, pf);
+    if (have_next) start_tile<C, I8>(S, nxt, sn, pf);
+    compute(sc, std::integral_constant<bool, I8 == 1>{});
+    if (have_next) finish_tile<C, I8>(nxt, sn, pf);
     __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of this thread have landed
     __syncthreads();
     cur = nxt;
     have = have_next;
   };
+  auto first_tile = [&](auto i8_tag) __attribute__((always_inline)) {
+    if (have) {
+      Prefetch<C> pf;
+      start_tile<C, decltype(i8_tag)::value>(S, cur, stage0, pf);
+      finish_tile<C, decltype(i8_tag)::value>(cur, stage0, pf);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // direct-to-LDS loads of this thread have landed
+    __syncthreads();
+  };
+  constexpr int I8_BF16 = HAS_I8 ? 2 : 0;
+  bool odd = false;  // the current tile sits in stage1
+  if constexpr (HAS_I8) {
+    // Phase 1: the INT8 tiles in fp16.  A tile whose scales do not fit fp16's
+    // range (|K| > 65,024 or |V| > 8.3e6 in the history) sends the block back
+    // to the start, to take every tile in bf16.
+    if (have && cur.src < SRC_TXT) {
+      to_f16_q();
+      first_tile(std::integral_constant<int, 1>{});
+      bool redo = false;
+      while (have && cur.src < SRC_TXT) {
+        if (!cur.ok16) { redo = true; break; }
+        step(stage0, stage1, std::integral_constant<int, 1>{});
+        if (!have || cur.src >= SRC_TXT) { odd = true; break; }
+        if (!cur.ok16) { redo = true; odd = true; break; }
+        step(stage1, stage0, std::integral_constant<int, 1>{});
+      }
+      // bf16 Q for what follows; every load of the last step has been waited
+      // for, so this wait covers only these
+      if (have || redo) {
+        load_q();
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if (redo) {
+        // start over: one softmax over every tile, INT8 ones staged in bf16
+#pragma unroll
+        for (int q = 0; q < QB; ++q) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[q][c] = f32x16{};
+          st[q].m = -INFINITY;
+          st[q].l = 0.0f;
+        }
+        e = 0;
+        sp = spans[0];
+        kpos = sp.k0;
+        have = next_tile(cur);
+        odd = false;
+        first_tile(std::integral_constant<int, I8_BF16>{});
+      }
+    } else {
+      first_tile(std::integral_constant<int, I8_BF16>{});
+    }
+  } else {
+    first_tile(std::integral_constant<int, I8_BF16>{});
+  }
+  // Phase 2: the bf16 tiles (and, after a restart, every tile)
+  if (have && odd) step(stage1, stage0, std::integral_constant<int, I8_BF16>{});
   while (have) {
-    step(stage0, stage1);
+    step(stage0, stage1, std::integral_constant<int, I8_BF16>{});
     if (!have) break;
-    step(stage1, stage0);
+    step(stage1, stage0, std::integral_constant<int, I8_BF16>{});
   }
 
   // epilogue: O = acc / l, lse = (m + log2 l) * ln 2; with key splits the
@@ -704,9 +873,17 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   if (p.n_tasks == 0) return hipSuccess;
   const int blocks = 8 * p.tasks_per_xcd;
   if (p.tile_rows == DenseCfg::ROWS) {
-    hipLaunchKernelGGL((seg_attn_fwd_kernel<DenseCfg, HN_DENSE_MINB>), dim3(blocks), dim3(DenseCfg::T), 0, s, p);
+    if (p.has_i8)
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<DenseCfg, HN_DENSE_MINB, true>), dim3(blocks), dim3(DenseCfg::T),
+                         0, s, p);
+    else
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<DenseCfg, HN_DENSE_MINB, false>), dim3(blocks), dim3(DenseCfg::T),
+                         0, s, p);
   } else if (p.tile_rows == SparseCfg::ROWS) {
-    hipLaunchKernelGGL((seg_attn_fwd_kernel<SparseCfg, 2>), dim3(blocks), dim3(SparseCfg::T), 0, s, p);
+    if (p.has_i8)
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<SparseCfg, 2, true>), dim3(blocks), dim3(SparseCfg::T), 0, s, p);
+    else
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<SparseCfg, 2, false>), dim3(blocks), dim3(SparseCfg::T), 0, s, p);
   } else {
     return hipErrorInvalidValue;
   }

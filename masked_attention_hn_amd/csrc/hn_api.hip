@@ -612,6 +612,7 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
   p.ring_cap = c->window_frames * P;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.txt_len = (int32_t)tl;
+  p.has_i8 = (c->head_tokens > 0 || kept_frames(c) > 0) ? 1 : 0;
   p.counts = static_cast<const int32_t*>(plan->dev);
   p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
                                               hn::plan_counts_bytes(p.n_vt));

@@ -124,6 +124,7 @@ struct AttnParams {
   int32_t ring_cap;      // ring stride (tokens) per head = W*P
   float scale_log2;      // sm_scale * log2(e)
   int32_t txt_len;       // h + sum(a) text rows of the current segment
+  int32_t has_i8;        // the plan may visit INT8 sources (history heads or ring frames)
   const int32_t* counts;
   const Span* spans;
   const __bf16* q;

@@ -69,6 +69,67 @@ def test_append_bitexact_and_ring_order(name):
     assert cache.frames_seen == sum(s.frames for s in w.segments[:w.query_segment])
 
 
+def _check_frames_and_heads(w, data, cache, appended, frames):
+    """Ring slots of the given global frames and the whole head store after
+    segments 0 .. appended-1 were appended, bit for bit against the oracle."""
+    P, Wf = w.segments[0].tokens_per_frame, w.ring_frames
+    src = []  # (segment, local frame) of every global frame
+    for s in range(appended):
+        src += [(s, f) for f in range(w.segments[s].frames)]
+    fs = len(src)
+    for g in frames:
+        assert fs - min(fs, Wf) <= g < fs, "frame not in the window"
+        s, f = src[g]
+        slot = g % Wf
+        for nm, codes, scales in (("k_vid", cache.ring_k, cache.ring_ks), ("v_vid", cache.ring_v, cache.ring_vs)):
+            q, sc = oracle.quantize(data["segments"][s][nm][f * P:(f + 1) * P])   # [P][H][D], [P][H]
+            got_q = codes[:, slot * P:(slot + 1) * P].cpu().numpy().transpose(1, 0, 2)
+            got_s = scales[:, slot * P:(slot + 1) * P].cpu().numpy().T
+            assert np.array_equal(got_q, q), f"{nm} codes of frame {g}"
+            assert np.array_equal(got_s.view(np.uint32), sc.view(np.uint32)), f"{nm} scales of frame {g}"
+    hoff = 0
+    for s in range(appended):
+        hl = w.segments[s].head_len
+        for nm, codes, scales in (("k_txt", cache.heads_k, cache.heads_ks), ("v_txt", cache.heads_v, cache.heads_vs)):
+            q, sc = oracle.quantize(data["segments"][s][nm][:hl])
+            got_q = codes[:, hoff:hoff + hl].cpu().numpy().transpose(1, 0, 2)
+            got_s = scales[:, hoff:hoff + hl].cpu().numpy().T
+            assert np.array_equal(got_q, q), f"{nm} codes of segment {s}"
+            assert np.array_equal(got_s.view(np.uint32), sc.view(np.uint32)), f"{nm} scales of segment {s}"
+        hoff += hl
+    assert cache.head_tokens == hoff and cache.frames_seen == fs
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5"])
+def test_append_bitexact_target_shapes(name):
+    """The appends of the five target configurations' shapes: the 480x832
+    segment itself (12,468 tokens x 16 heads, no window: every frame checked);
+    three 1280x704 segments through the 18-frame window (every kept frame:
+    30-frame segments wrap the ring); six 1280x704 segments with 1,280-token
+    heads and no window (a spread of 24 of the 180 frames, first and last of
+    every segment included).  All heads of the head store are checked."""
+    print(f"[quant] {name}", flush=True)
+    w = W.config(name)
+    data = W.generate(w)
+    cache = G.new_cache(w)
+    if w.query_segment == 0:
+        appended = 1
+        seg = w.segments[0]
+        d = data["segments"][0]
+        hn.hn_kv_quant_append(cache, G.layout(0, seg), G.dev(d["k_txt"]), G.dev(d["v_txt"]),
+                              G.dev(d["k_vid"]), G.dev(d["v_vid"]))
+    else:
+        appended = w.query_segment
+        G.fill_history(w, data, cache)
+    torch.cuda.synchronize()
+    fs = sum(s.frames for s in w.segments[:appended])
+    kept = list(range(fs - min(fs, w.ring_frames), fs))
+    if len(kept) > 30:
+        ends = [g for s in range(appended) for g in (30 * s, 30 * s + 29)]
+        kept = sorted(set(ends + kept[::15]))
+    _check_frames_and_heads(w, data, cache, appended, kept)
+
+
 def _append_rows(rows_bits: np.ndarray, H: int = 16):
     """Append rows [n][128] as one segment (F=1, P=n/H tokens, heads inner) and
     return (codes [n][128], scales [n]) read back from the ring."""

@@ -25,7 +25,7 @@ def data_of(name):
 
 @pytest.mark.parametrize("name,rows_env", [(n, "auto") for n in
                                            ("c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4",
-                                            "c2", "c3", "c5")] +
+                                            "c2", "c3", "c4", "c5")] +
                          [(n, "128") for n in ("c1", "m1", "m2", "m4", "c2")])
 def test_dense_mask_matches_oracle(name, rows_env, monkeypatch):
     # the spans are built per plan tile; both tile heights must expand to the oracle mask
@@ -36,7 +36,7 @@ def test_dense_mask_matches_oracle(name, rows_env, monkeypatch):
     d = data_of(name)
     run = G.Run(w, d)
     nq = w.current.video_len
-    rows = np.arange(nq) if nq <= 2048 else G.sample_rows(nq, 300, seed=1)
+    rows = np.arange(nq) if nq <= 2048 else G.sample_rows(nq)
     csr = d.get("csr") if w.sparse_keep is not None else None
     ref_full = oracle.mask(w, rows, csr)
     cols = G.canonical_columns(w)

@@ -1,15 +1,15 @@
 """GPU parity of hn_seg_attn_fwd against the fp64 oracle.
 
-Bar on unit-variance normal inputs: max-abs error <= 2e-2 and mean-abs error
-<= 2e-3 (both sides use the same INT8 history, so the tolerance covers bf16
-rounding of the probabilities, the accumulation order and the bf16 output).
-Heavy-tailed (Student-t) keys and values concentrate some rows on a few keys,
-and |O| then reaches 5-20: the bf16 output alone is off by up to 2^-8 |O| and
-the bf16 probabilities by about 2^-9 |O|, which no bf16-output kernel can keep
-under 2e-2 once |O| >= 8.  Heavy-tailed cases are therefore held to
-|err| <= 2e-2 + 2^-7 |O_ref| elementwise, with the same mean-abs bar.
-Small layouts are compared on every row; the full-size target shapes on rows
-sampled across every tile, computed by the oracle against all keys.
+Bar (tests/_gpu.py): max-abs error <= 2e-2 and mean-abs error <= 2e-3 on
+unit-variance inputs, normal and heavy-tailed (Student-t) alike; elements
+with |O_ref| >= 8, where the bf16 output's own rounding reaches 2^-5, may
+also carry half a bf16 unit in the last place.  Both sides use the same INT8
+history values, so the bar covers the kernel's 16-bit operands (bf16 for the
+segment's own keys and values, fp16 for the dequantized history), the
+16-bit probabilities, the accumulation order and the bf16 output.
+Small layouts are compared on every row; c2 and c5 on every row too; the
+other full-size shapes on the first, middle and last row of every 128-row
+query tile, computed by the oracle against all keys.
 """
 import math
 
@@ -26,8 +26,6 @@ if torch.cuda.is_available():
     import masked_attention_hn_amd as hn
     import _gpu as G
 
-MAX_ABS = 2e-2
-MEAN_ABS = 2e-3
 _DATA = {}
 
 
@@ -37,24 +35,16 @@ def data_of(name):
     return _DATA[name]
 
 
-NORMAL = ("c1", "c1_evict", "c1_future", "c2", "c3", "c5", "c3_h2", "m1", "m3", "m4")
-
-
-def _compare(w, d, run, rows):
+def _compare(w, d, run, rows, kv=None):
     o, lse = run.attn()
     o = o.float().cpu().numpy()[rows]
     lse = lse.cpu().numpy()[:, rows]
-    ref, ref_lse, _ = oracle.attention(w, d, rows)
+    ref, ref_lse, _ = oracle.attention(w, d, rows, kv=kv)
     err = np.abs(o - ref)
     i = np.unravel_index(np.argmax(err), err.shape)
     print(f"  max-abs {err.max():.3e} (|O_ref| there {abs(ref[i]):.3f}, row {rows[i[0]]}) "
           f"mean-abs {err.mean():.3e} lse max-abs {np.abs(lse - ref_lse).max():.3e}", flush=True)
-    if w.name in NORMAL:
-        assert w.kv_dist == "normal"
-        assert err.max() <= MAX_ABS
-    else:
-        assert np.all(err <= MAX_ABS + 2.0 ** -7 * np.abs(ref))
-    assert err.mean() <= MEAN_ABS
+    G.check_bar(o, ref, w.name)
     assert np.abs(lse - ref_lse).max() <= 1e-2
     assert np.all(np.isfinite(o))
 
@@ -74,16 +64,26 @@ def test_attention_small_all_rows(name, rows, monkeypatch):
     _compare(w, d, run, np.arange(w.current.video_len))
 
 
-@pytest.mark.parametrize("name", ["c2", "c3", "c5", "c3_h2", "c4"])
+@pytest.mark.parametrize("name", ["c3", "c3_h2", "c4"])
 def test_attention_full_size_sampled_rows(name):
     print(f"[attn] {name}", flush=True)
     w = W.config(name)
     d = data_of(name)
     run = G.Run(w, d)
-    rows = G.sample_rows(w.current.video_len, 160 if name == "c4" else 256, seed=2)
+    rows = G.sample_rows(w.current.video_len)
     _compare(w, d, run, rows)
     if name == "c4":
         _DATA.pop(name)
+
+
+@pytest.mark.parametrize("name", ["c2", "c5"])
+def test_attention_full_size_all_rows(name):
+    # the 480x832 segment (dense and keep list): every one of its 11,700 rows
+    print(f"[attn] {name} all rows", flush=True)
+    w = W.config(name)
+    d = data_of(name)
+    run = G.Run(w, d)
+    _compare(w, d, run, np.arange(w.current.video_len))
 
 
 @pytest.mark.parametrize("name", ["m2", "m4", "c2", "c5"])

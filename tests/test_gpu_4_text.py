@@ -3,8 +3,8 @@ tokens as queries, in the same hn_seg_attn_fwd call as the video queries).
 
 Mask: the DENSE rows past the video rows must equal the oracle's mask_text
 bit for bit.  Attention: the same bar as the video queries (max-abs <= 2e-2
-and mean-abs <= 2e-3 on unit-variance normal inputs; heavy-tailed inputs
-elementwise 2e-2 + 2^-7 |O_ref|).  Adding the text queries must leave the
+and mean-abs <= 2e-3 on unit-variance inputs; elements with |O_ref| >= 8 may
+also carry half a bf16 unit in the last place: tests/_gpu.py).  Adding the text queries must leave the
 video outputs bit-identical, and tails a text query cannot see must not
 change its output at all.
 """
@@ -20,9 +20,6 @@ pytestmark = pytest.mark.gpu
 if torch.cuda.is_available():
     import _gpu as G
 
-MAX_ABS = 2e-2
-MEAN_ABS = 2e-3
-NORMAL = ("c1", "c1_evict", "c1_future", "c2", "c3", "m1", "m3", "m4")
 _DATA = {}
 
 
@@ -54,11 +51,7 @@ def _check(w, d, o_txt, lse_txt, rows):
     err = np.abs(o - ref)
     print(f"  text max-abs {err.max():.3e} mean-abs {err.mean():.3e} "
           f"lse max-abs {np.abs(lse - ref_lse).max():.3e}", flush=True)
-    if w.name in NORMAL:
-        assert err.max() <= MAX_ABS
-    else:
-        assert np.all(err <= MAX_ABS + 2.0 ** -7 * np.abs(ref))
-    assert err.mean() <= MEAN_ABS
+    G.check_bar(o, ref, f"{w.name} text")
     assert np.abs(lse - ref_lse).max() <= 1e-2
     assert np.all(np.isfinite(o))
 
@@ -73,7 +66,7 @@ def test_text_attention(name):
     o, o_txt, lse, lse_txt = run.attn_joint()
     tl = w.current.text_len
     if name == "c4":
-        rows = G.sample_rows(tl, 96, seed=4)
+        rows = G.sample_rows(tl, tile=32)
     else:
         rows = np.arange(tl)
     _check(w, d, o_txt, lse_txt, rows)

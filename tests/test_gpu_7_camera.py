@@ -32,7 +32,7 @@ def test_camera_attention(name, radius):
     torch.cuda.synchronize()
     got = o.float().cpu().numpy()
     nq = w.current.video_len
-    rows = np.arange(nq) if nq <= 4096 else G.sample_rows(nq, 2048, seed=7)
+    rows = np.arange(nq) if nq <= 4096 else G.sample_rows(nq, tile=16)
     if radius == 0:
         P = w.current.tokens_per_frame
         v = W.bf16_bits_to_f32(d["v_cam"])

@@ -41,12 +41,7 @@ CASES = {
 
 
 def _bar(w, got, ref):
-    err = np.abs(got - ref)
-    if w.kv_dist == "normal":
-        assert err.max() <= 2e-2
-    else:
-        assert np.all(err <= 2e-2 + 2.0 ** -7 * np.abs(ref))
-    assert err.mean() <= 2e-3
+    G.check_bar(got, ref, w.name)
 
 
 @pytest.mark.parametrize("name", list(CASES))
