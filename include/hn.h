@@ -89,7 +89,9 @@ typedef struct hn_seg_layout {
 /* The INT8 KV cache of earlier segments.
  *
  * Keys and values are stored as INT8 with one fp32 scale per (token, head)
- * and used in BF16 ([T] "单卡 4090 怎么做到的", first technique).  Video of
+ * and computed in 16-bit floating point ([T] "单卡 4090 怎么做到的", first
+ * technique: INT8 storage, BF16 compute; see hn_seg_attn_fwd for the 16-bit
+ * type the history takes).  Video of
  * earlier segments lives in a ring of W latent frames, oldest frame evicted
  * first ([T] same section, second technique: 18 history frames; [H]
  * configuration table, history row).  Description heads of every earlier
@@ -238,6 +240,18 @@ typedef struct hn_block_sparse {
 
 typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
 
+/* Optional choices of a tile plan (host memory, read during the call).  A
+ * NULL pointer, or 0 in a field, leaves the choice to the library (below).
+ * They exist for tuning and testing; every value gives the same attention up
+ * to rounding. */
+typedef struct hn_plan_opts {
+  int32_t n_splits;           /* key splits per video query tile: 0 = automatic, else 1 .. 16 */
+  int32_t n_splits_text;      /* key splits per text query tile: 0 = automatic, else 1 .. 16 */
+  int32_t tile_rows;          /* query rows per tile of a plan without keep list: 0 = automatic
+                                 (256), 128 or 256; plans with a keep list always use HN_TILE */
+  int32_t reserved0;          /* must be 0 */
+} hn_plan_opts;
+
 /* Tile plan for one (cache state, segment, keep list); filled by
  * hn_attn_mask_build in TILE_PLAN mode and consumed by hn_seg_attn_fwd.
  * It may be reused by every attention call of the segment (all blocks and
@@ -250,14 +264,13 @@ typedef enum { HN_MASK_TILE_PLAN = 0, HN_MASK_DENSE = 1 } hn_mask_mode;
  * ranges that run as separate blocks; each writes a partial result into the
  * workspace and a merge kernel combines them (one softmax, exactly as
  * without the split up to rounding).  The split count comes from the
- * device's compute-unit count and the layout; HN_ATTN_SPLITS=n in the
- * environment forces n (1..16).  Text query tiles, which follow all video
- * tiles in a joint launch, get their own count: the one (of 1, 2, 4, 8, 16)
- * with the least estimated makespan when the blocks are dealt to the slots
- * in order, so that they fill what the video blocks leave free; tiles of
- * fewer than 4096 keys stay whole (HN_ATTN_TEXT_SPLITS=n forces n).  Dense
- * plans use 256-row query tiles (HN_ATTN_DENSE_ROWS=128 forces 128-row
- * ones).  With n_splits > 1
+ * device's compute-unit count and the layout (opts->n_splits forces one).
+ * Text query tiles, which follow all video tiles in a joint launch, get
+ * their own count: the one (of 1, 2, 4, 8, 16) with the least estimated
+ * makespan when the blocks are dealt to the slots in order, so that they
+ * fill what the video blocks leave free; tiles of fewer than 4096 keys stay
+ * whole (opts->n_splits_text forces a count).  Dense plans use 256-row
+ * query tiles (opts->tile_rows = 128 gives 128-row ones).  With n_splits > 1
  * attention calls that share one plan workspace must not overlap in time
  * (same stream, or ordered), since they write its partial area. */
 typedef struct hn_tile_plan {
@@ -277,11 +290,11 @@ typedef struct hn_tile_plan {
   int32_t reserved0;
 } hn_tile_plan;
 
-/* Workspace bytes TILE_PLAN mode needs (0 on invalid arguments): the span
- * lists, plus, with split-KV, H x tiles x splits x tile_q x (128 + 1) floats
- * of partial results. */
+/* Workspace bytes TILE_PLAN mode needs with the same opts (0 on invalid
+ * arguments): the span lists, plus, with split-KV, H x tiles x splits x
+ * tile_q x (128 + 1) floats of partial results. */
 size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg,
-                              const hn_block_sparse* sparse);
+                              const hn_block_sparse* sparse, const hn_plan_opts* opts);
 
 /* Build the attention mask of the current segment's queries.
  *
@@ -302,6 +315,9 @@ size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg
  * of tail j sees tail j and no other tail, a head token sees no tail.  Keep
  * lists concern video query tiles only; text queries attend densely.
  *
+ * opts (nullable): split counts and tile height (hn_plan_opts); in DENSE mode
+ *   only tile_rows matters (the expansion is the same for every height).
+ *   Invalid values give HN_ERR_INVALID.
  * TILE_PLAN: `out` is the workspace (>= hn_attn_workspace_size bytes, device,
  *   16-byte aligned).  For every query tile a kernel writes the list of key
  *   spans to visit, each classified against the tile's rows as full or
@@ -317,7 +333,7 @@ size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg
  *   must be NULL.
  */
 hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
-                             const hn_block_sparse* sparse, hn_mask_mode mode,
+                             const hn_block_sparse* sparse, const hn_plan_opts* opts, hn_mask_mode mode,
                              int32_t row0, int32_t nrows, void* out, size_t out_bytes,
                              hn_tile_plan* plan, hipStream_t stream);
 
@@ -328,8 +344,13 @@ hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
  *   O[q] = sum_k softmax_k(sm_scale * Q[q].K[k]) V[k]
  * History keys/values are the dequantized INT8 values q*scale; the segment's
  * own keys/values are used as given (quantization is storage-only,
- * [T] "单卡 4090 怎么做到的", first technique).  BF16 MFMA, fp32 accumulation
- * and online softmax.
+ * [T] "单卡 4090 怎么做到的", first technique).  16-bit MFMA with fp32
+ * accumulation and online softmax: the segment's own tiles in BF16 (its
+ * inputs' type); the history tiles in FP16 (q*scale correctly rounded to 11
+ * significant bits, against an FP16 copy of Q), which keeps the history as
+ * close to q*scale as the segment's own values are to their inputs.  The
+ * FP16 path holds history values with |K| <= 65,024 and |V| <= 8.3e6; a tile
+ * outside that range sends its query tile through BF16 for every key.
  *
  * plan         : from hn_attn_mask_build(TILE_PLAN) for this exact cache
  *                state and segment, workspace still intact; else HN_ERR_ORDER

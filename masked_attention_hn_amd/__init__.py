@@ -11,8 +11,9 @@ The exported functions carry the C names:
     hn_attn_workspace_size, hn_kv_cache_sizes, hn_kv_cache_reset,
     hn_kv_archive_evict, hn_kv_cache_rewind, hn_camera_attn_fwd,
     hn_status_string, hn_last_error
-plus small helpers (KVCache, KVArchive, SegLayout, BlockSparse, build_plan,
-dense_mask, seg_attn, seg_attn_joint) that own the buffers those calls need.
+plus small helpers (KVCache, KVArchive, SegLayout, BlockSparse, PlanOpts,
+build_plan, dense_mask, seg_attn, seg_attn_joint) that own the buffers those
+calls need.
 """
 from __future__ import annotations
 
@@ -24,8 +25,7 @@ from typing import Optional, Sequence
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# HN_LIB may point at another build of the same library (used to compare builds)
-LIB_PATH = os.environ.get("HN_LIB") or os.path.join(_PKG, "libhn.so")
+LIB_PATH = os.path.join(_PKG, "libhn.so")
 
 HEAD_DIM = 128
 MAX_ACTIONS = 64
@@ -67,6 +67,11 @@ class hn_block_sparse(ctypes.Structure):
                 ("row_ptr", _vp), ("col", _vp)]
 
 
+class hn_plan_opts(ctypes.Structure):
+    _fields_ = [("n_splits", ctypes.c_int32), ("n_splits_text", ctypes.c_int32),
+                ("tile_rows", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
+
+
 class hn_tile_plan(ctypes.Structure):
     _fields_ = [("dev", _vp), ("tile_q", ctypes.c_int32), ("n_qtiles", ctypes.c_int32),
                 ("n_text_tiles", ctypes.c_int32), ("max_spans", ctypes.c_int32),
@@ -96,10 +101,11 @@ _lib.hn_kv_quant_append.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(
                                     _vp, _vp, _vp, _vp, _vp]
 _lib.hn_kv_quant_append.restype = _S
 _lib.hn_attn_workspace_size.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
-                                        ctypes.POINTER(hn_block_sparse)]
+                                        ctypes.POINTER(hn_block_sparse), ctypes.POINTER(hn_plan_opts)]
 _lib.hn_attn_workspace_size.restype = ctypes.c_size_t
 _lib.hn_attn_mask_build.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
-                                    ctypes.POINTER(hn_block_sparse), _S, ctypes.c_int32,
+                                    ctypes.POINTER(hn_block_sparse), ctypes.POINTER(hn_plan_opts),
+                                    _S, ctypes.c_int32,
                                     ctypes.c_int32, _vp, ctypes.c_size_t,
                                     ctypes.POINTER(hn_tile_plan), _vp]
 _lib.hn_attn_mask_build.restype = _S
@@ -313,8 +319,18 @@ def _sp(sparse: Optional[BlockSparse]):
     return ctypes.byref(sparse.c) if sparse is not None else None
 
 
-def hn_attn_workspace_size(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None) -> int:
-    n = _lib.hn_attn_workspace_size(ctypes.byref(cache.c), ctypes.byref(seg.c), _sp(sparse))
+def PlanOpts(n_splits: int = 0, n_splits_text: int = 0, tile_rows: int = 0) -> hn_plan_opts:
+    """Plan choices for hn_attn_mask_build / hn_attn_workspace_size (0 = automatic)."""
+    return hn_plan_opts(n_splits, n_splits_text, tile_rows, 0)
+
+
+def _op(opts: Optional[hn_plan_opts]):
+    return ctypes.byref(opts) if opts is not None else None
+
+
+def hn_attn_workspace_size(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None,
+                           opts: Optional[hn_plan_opts] = None) -> int:
+    n = _lib.hn_attn_workspace_size(ctypes.byref(cache.c), ctypes.byref(seg.c), _sp(sparse), _op(opts))
     if n == 0:
         raise HNError(HN_ERR_INVALID, hn_last_error())
     return n
@@ -322,9 +338,9 @@ def hn_attn_workspace_size(cache: KVCache, seg: SegLayout, sparse: Optional[Bloc
 
 def hn_attn_mask_build(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse], mode: int,
                        row0: int, nrows: int, out: torch.Tensor, plan: Optional[hn_tile_plan],
-                       stream=None):
-    _check(_lib.hn_attn_mask_build(ctypes.byref(cache.c), ctypes.byref(seg.c), _sp(sparse), mode,
-                                   row0, nrows, _ptr(out), out.numel() * out.element_size(),
+                       stream=None, opts: Optional[hn_plan_opts] = None):
+    _check(_lib.hn_attn_mask_build(ctypes.byref(cache.c), ctypes.byref(seg.c), _sp(sparse), _op(opts),
+                                   mode, row0, nrows, _ptr(out), out.numel() * out.element_size(),
                                    ctypes.byref(plan) if plan is not None else None,
                                    _stream(stream)))
 
@@ -346,24 +362,26 @@ class Plan:
 
 
 def build_plan(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None,
-               workspace: Optional[torch.Tensor] = None, stream=None) -> Plan:
-    n = hn_attn_workspace_size(cache, seg, sparse)
+               workspace: Optional[torch.Tensor] = None, stream=None,
+               opts: Optional[hn_plan_opts] = None) -> Plan:
+    n = hn_attn_workspace_size(cache, seg, sparse, opts)
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(n, dtype=torch.uint8, device="cuda")
     c = hn_tile_plan()
-    hn_attn_mask_build(cache, seg, sparse, HN_MASK_TILE_PLAN, 0, 0, workspace, c, stream)
+    hn_attn_mask_build(cache, seg, sparse, HN_MASK_TILE_PLAN, 0, 0, workspace, c, stream, opts)
     return Plan(workspace, c)
 
 
 def dense_mask(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse] = None,
-               row0: int = 0, nrows: Optional[int] = None, stream=None) -> torch.Tensor:
+               row0: int = 0, nrows: Optional[int] = None, stream=None,
+               opts: Optional[hn_plan_opts] = None) -> torch.Tensor:
     """Rows [0, video_len) are the video queries, [video_len, video_len + text_len)
     the text queries."""
     nrows = seg.video_len - row0 if nrows is None else nrows
     kept = min(cache.frames_seen, cache.c.window_frames)
     lk = cache.head_tokens + kept * cache.c.tokens_per_frame + seg.text_len + seg.video_len
     out = torch.empty((max(nrows, 1), lk), dtype=torch.uint8, device="cuda")
-    hn_attn_mask_build(cache, seg, sparse, HN_MASK_DENSE, row0, nrows, out, None, stream)
+    hn_attn_mask_build(cache, seg, sparse, HN_MASK_DENSE, row0, nrows, out, None, stream, opts)
     return out[:nrows]
 
 

@@ -107,13 +107,8 @@ int device_cus() {
 // r_2 / 2 + 1/4 < r_1 and each half keeps at least 8192 keys.  A grid of at
 // most one block per two CUs is split to about one block per CU, with no
 // fewer than 1024 keys per split.  blocks_per_cu is how many blocks of the
-// plan's tile height share a CU.  HN_ATTN_SPLITS=n in the environment forces
-// n (tuning and tests).
+// plan's tile height share a CU.
 int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu) {
-  if (const char* e = std::getenv("HN_ATTN_SPLITS")) {
-    const int v = std::atoi(e);
-    if (v >= 1 && v <= HN_MAX_SPLITS) return v;
-  }
   const int64_t cus = device_cus();
   const int64_t tasks = (int64_t)H * n_qtiles;
   if (tasks <= 0) return 1;
@@ -142,13 +137,8 @@ int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu)
 // splits (the 2-head share's 10 text tiles run whole beside its 208 video
 // blocks).  Text tiles with
 // fewer than 4096 keys are not split, and pieces keep at least 1,024 keys.
-// HN_ATTN_TEXT_SPLITS=n forces n.
 int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, int n_text_tiles,
                        int64_t keys_per_tile, int blocks_per_cu) {
-  if (const char* e = std::getenv("HN_ATTN_TEXT_SPLITS")) {
-    const int v = std::atoi(e);
-    if (v >= 1 && v <= HN_MAX_SPLITS) return v;
-  }
   if (n_text_tiles <= 0 || keys_per_tile < 4096) return 1;
   constexpr double kOverhead = 1600.0;
   const int64_t slots = std::max<int64_t>(device_cus() * std::max(blocks_per_cu, 1), 1);
@@ -185,28 +175,45 @@ int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, 
 // leave compute units idle: in one run the 2-head share above took
 // 1.215-1.217 ms with 208 such blocks against 1.464 ms with 414 128-row
 // blocks, and 1.45-1.47 against 1.67-1.68 ms with its text queries).
-// HN_ATTN_DENSE_ROWS=128|256 in the environment forces the height (tuning, tests).
-int plan_tile_rows(bool sparse) {
+// opts->tile_rows = 128 gives the 128-row tiles (tuning, tests).
+int plan_tile_rows(bool sparse, const hn_plan_opts* o) {
   if (sparse) return HN_TILE;
-  const int rows = hn::attn_dense_rows();
-  if (const char* e = std::getenv("HN_ATTN_DENSE_ROWS")) {
-    const int v = std::atoi(e);
-    if (v == HN_TILE || v == rows) return v;
-  }
-  return rows;
+  if (o && o->tile_rows == HN_TILE) return HN_TILE;
+  return hn::attn_dense_rows();
 }
 
-// Plan parameters for the current state; validates the keep list.
+// A plan's query-tile height is one the attention kernel has an instance for.
+bool valid_tile_rows(int rows, bool sparse) {
+  return sparse ? rows == HN_TILE : (rows == HN_TILE || rows == hn::attn_dense_rows());
+}
+
+hn_status check_opts(const hn_plan_opts* o, bool sparse) {
+  if (!o) return HN_OK;
+  if (o->n_splits < 0 || o->n_splits > HN_MAX_SPLITS || o->n_splits_text < 0 ||
+      o->n_splits_text > HN_MAX_SPLITS)
+    return fail(HN_ERR_INVALID, "split counts %d / %d outside [0, %d]", o->n_splits, o->n_splits_text,
+                HN_MAX_SPLITS);
+  if (o->tile_rows != 0 && o->tile_rows != HN_TILE && o->tile_rows != hn::attn_dense_rows())
+    return fail(HN_ERR_INVALID, "tile_rows %d is not 0, %d or %d", o->tile_rows, HN_TILE,
+                hn::attn_dense_rows());
+  if (sparse && o->tile_rows != 0 && o->tile_rows != HN_TILE)
+    return fail(HN_ERR_INVALID, "a keep list fixes %d-row query tiles", HN_TILE);
+  if (o->reserved0 != 0) return fail(HN_ERR_INVALID, "hn_plan_opts.reserved0 must be 0");
+  return HN_OK;
+}
+
+// Plan parameters for the current state; validates the keep list and opts.
 hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
-                           hn::PlanParams* pp) {
+                           const hn_plan_opts* opts, hn::PlanParams* pp) {
   int64_t tl = 0;
   hn_status st = check_cache(c);
   if (st != HN_OK) return st;
   if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  if ((st = check_opts(opts, sp != nullptr)) != HN_OK) return st;
   std::memset(pp, 0, sizeof(*pp));
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  pp->tile_q = plan_tile_rows(sp != nullptr);
+  pp->tile_q = plan_tile_rows(sp != nullptr, opts);
   pp->n_qtiles = (int)ceil_div(lq, pp->tile_q);
   pp->n_text_tiles = (int)ceil_div(tl, pp->tile_q);
   pp->lq = lq;
@@ -235,12 +242,17 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     int64_t video = (int64_t)pp->ring_tokens + lq;
     if (sp && sp->row_ptr && pp->n_qtiles > 0) video = video / 4;
     // dense 256-row blocks run one per CU, 128-row blocks two
-    pp->n_splits = choose_splits(c->num_heads, pp->n_qtiles, keys + video, pp->tile_q >= 256 ? 1 : 2);
+    pp->n_splits = (opts && opts->n_splits > 0)
+                       ? opts->n_splits
+                       : choose_splits(c->num_heads, pp->n_qtiles, keys + video, pp->tile_q >= 256 ? 1 : 2);
     // text queries see heads, the whole ring and the own video (no keep list)
     const int bpc = pp->tile_q >= 256 ? 1 : 2;
-    pp->n_splits_text = choose_text_splits(c->num_heads, (int64_t)c->num_heads * pp->n_qtiles * pp->n_splits,
-                                           (keys + video) / pp->n_splits, pp->n_text_tiles,
-                                           keys + (int64_t)pp->ring_tokens + lq, bpc);
+    pp->n_splits_text = (opts && opts->n_splits_text > 0)
+                            ? opts->n_splits_text
+                            : choose_text_splits(c->num_heads,
+                                                 (int64_t)c->num_heads * pp->n_qtiles * pp->n_splits,
+                                                 (keys + video) / pp->n_splits, pp->n_text_tiles,
+                                                 keys + (int64_t)pp->ring_tokens + lq, bpc);
   }
   int max_spans = 4 + s->num_actions;
   if (sp) {
@@ -477,17 +489,18 @@ hn_status hn_kv_cache_rewind(hn_kv_cache* c, hn_kv_archive* a, int64_t frames_se
   return ok();
 }
 
-size_t hn_attn_workspace_size(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp) {
+size_t hn_attn_workspace_size(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
+                              const hn_plan_opts* opts) {
   hn::PlanParams pp;
-  if (make_plan_params(c, s, sp, &pp) != HN_OK) return 0;
+  if (make_plan_params(c, s, sp, opts, &pp) != HN_OK) return 0;
   return plan_ws_bytes(c, pp);
 }
 
 hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
-                             hn_mask_mode mode, int32_t row0, int32_t nrows, void* out, size_t out_bytes,
-                             hn_tile_plan* plan, hipStream_t stream) {
+                             const hn_plan_opts* opts, hn_mask_mode mode, int32_t row0, int32_t nrows,
+                             void* out, size_t out_bytes, hn_tile_plan* plan, hipStream_t stream) {
   hn::PlanParams pp;
-  hn_status st = make_plan_params(c, s, sp, &pp);
+  hn_status st = make_plan_params(c, s, sp, opts, &pp);
   if (st != HN_OK) return st;
   if (!out) return fail(HN_ERR_NULL, "output buffer is NULL");
   if (mode == HN_MASK_TILE_PLAN) {
@@ -569,10 +582,10 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
     return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  const int want_tile = plan_tile_rows(plan->sparse != 0);
+  const int tq = plan->tile_q;
   if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
-      plan->head_tokens != c->head_tokens || plan->tile_q != want_tile ||
-      plan->n_qtiles != (int)ceil_div(lq, want_tile) || plan->n_text_tiles != (int)ceil_div(tl, want_tile) ||
+      plan->head_tokens != c->head_tokens || !valid_tile_rows(tq, plan->sparse != 0) ||
+      plan->n_qtiles != (int)ceil_div(lq, tq) || plan->n_text_tiles != (int)ceil_div(tl, tq) ||
       plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS || plan->n_splits_text < 1 ||
       plan->n_splits_text > HN_MAX_SPLITS)
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");

@@ -40,8 +40,9 @@ class Run:
     """Cache filled with the history of a workload, a plan for the query segment,
     and the query segment's inputs on the GPU."""
 
-    def __init__(self, w: W.Workload, data: dict, use_sparse: bool = True):
+    def __init__(self, w: W.Workload, data: dict, use_sparse: bool = True, opts=None):
         self.w = w
+        self.opts = opts
         self.data = data
         self.cache = new_cache(w)
         fill_history(w, data, self.cache)
@@ -53,7 +54,7 @@ class Run:
         self.q = dev(data["q_vid"])
         self.q_txt = dev(data["q_txt"]) if w.current.text_len > 0 else None
         self.sparse = sparse_of(w, data) if use_sparse else None
-        self.plan = hn.build_plan(self.cache, self.seg, self.sparse)
+        self.plan = hn.build_plan(self.cache, self.seg, self.sparse, opts=opts)
 
     def attn(self, with_lse=True):
         out = hn.seg_attn(self.cache, self.seg, self.plan, self.q, self.k_txt, self.v_txt,
@@ -69,7 +70,7 @@ class Run:
         return out
 
     def dense(self, row0=0, nrows=None):
-        m = hn.dense_mask(self.cache, self.seg, self.sparse, row0, nrows)
+        m = hn.dense_mask(self.cache, self.seg, self.sparse, row0, nrows, opts=self.opts)
         torch.cuda.synchronize()
         return m.cpu().numpy().astype(bool)
 

@@ -97,32 +97,32 @@ def test_failed_launch_leaves_cache_unchanged():
 def test_workspace_sizes_and_plan_checks():
     c = fake_cache()
     s = seg_c()
-    n = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    n = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None, None)
     # counts padded to 256 bytes + (one video + one text query tile) x (4 + 2 tails)
     # spans of 32 bytes, padded to 256 bytes (4 query tiles of 2 heads: no key split)
     assert n == 256 + 512
     assert 256 + 2 * 6 * 32 <= n
     bad = hn.hn_block_sparse(64, 64, 1, 0, FAKE, FAKE)
-    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad)) == 0
+    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(bad), None) == 0
     sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
-    n_sp = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(sp))
+    n_sp = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), ctypes.byref(sp), None)
     assert n_sp == 256 + 2 * (4 + 2 + 0 + 1 + 1) * 32   # already a multiple of 256
     plan = hn.hn_tile_plan()
     build = hn._lib.hn_attn_mask_build
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n - 1,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 0, 0, 0, FAKE, n - 1,
                  ctypes.byref(plan), None) == hn.HN_ERR_WORKSPACE
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE + 4, n,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 0, 0, 0, FAKE + 4, n,
                  ctypes.byref(plan), None) == hn.HN_ERR_INVALID                # misaligned
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 0, 0, 0, FAKE, n, None,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 0, 0, 0, FAKE, n, None,
                  None) == hn.HN_ERR_NULL
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * 1000,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 1, 0, 48, FAKE, 48 * 1000,
                  ctypes.byref(plan), None) == hn.HN_ERR_INVALID                # plan in DENSE
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 40, 41, FAKE, 10 ** 6, None,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 1, 40, 41, FAKE, 10 ** 6, None,
                  None) == hn.HN_ERR_INVALID                    # rows past F*P + h + sum(a)
     lk = 0 + 0 + 32 + 48
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 1, 0, 48, FAKE, 48 * lk - 1, None,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 1, 0, 48, FAKE, 48 * lk - 1, None,
                  None) == hn.HN_ERR_WORKSPACE
-    assert build(ctypes.byref(c), ctypes.byref(s.c), None, 7, 0, 0, FAKE, n,
+    assert build(ctypes.byref(c), ctypes.byref(s.c), None, None, 7, 0, 0, FAKE, n,
                  None, None) == hn.HN_ERR_INVALID
 
 
@@ -137,12 +137,17 @@ def test_attention_rejects_stale_plan():
     out = [FAKE, None, None, None]  # o_vid, o_txt, lse, lse_txt
     call = lambda seg, pl, qq=q, oo=out, scale=0.1: fwd(ctypes.byref(c), ctypes.byref(seg.c), pl,
                                                         *qq, *kv, *oo, scale, None)
-    # the query-tile height of dense plans is the kernel's choice: a plan with
-    # the right one gets past the staleness check to the scale check
+    # dense plans come in the heights the kernel has instances for (128 and
+    # its default 256): a plan with one of them gets past the staleness check
+    # to the scale check
     tiles = [t for t in (64, 128, 256, 512)
              if (setattr(plan, "tile_q", t), call(s, ctypes.byref(plan), scale=float("nan")))[1]
              == hn.HN_ERR_INVALID]
-    assert len(tiles) == 1
+    assert tiles == [128, 256]
+    plan.sparse = 1                # a keep-list plan is always 128 rows
+    plan.tile_q = 256
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.sparse = 0
     plan.tile_q = tiles[0]
     plan.frames_seen = 24          # built for another cache state
     assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
@@ -177,14 +182,22 @@ def test_cache_sizes():
         hn.hn_kv_cache_sizes(0, 18, 880, 0)
 
 
-def test_split_count_forced_and_sized(monkeypatch):
-    """HN_ATTN_SPLITS forces the key split; the workspace then also holds the
-    partial results: H x virtual tiles x 128 rows x (128 + 1) floats."""
+def ws_size(c, seg, sparse=None, n_splits=0, n_splits_text=0, tile_rows=0):
+    """hn_attn_workspace_size with plan options (0 = automatic)."""
+    opts = hn.PlanOpts(n_splits, n_splits_text, tile_rows)
+    return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c),
+                                          ctypes.byref(sparse) if sparse is not None else None,
+                                          ctypes.byref(opts))
+
+
+def test_split_count_forced_and_sized():
+    """opts.n_splits forces the key split; the workspace then also holds the
+    partial results: H x virtual tiles x tile rows x (128 + 1) floats."""
     c = fake_cache()
     s = seg_c()
-    n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
-    monkeypatch.setenv("HN_ATTN_SPLITS", "3")
-    n3 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None, None)
+    assert ws_size(c, s) == n1                 # zeroed options = automatic = NULL options
+    n3 = ws_size(c, s, n_splits=3)
     vt = 1 * 3 + 1 * 1                         # video tile x 3 splits + text tile (80 keys: unsplit)
     spans = -(-(256 + vt * 6 * 32) // 256) * 256
     a256 = lambda b: -(-b // 256) * 256
@@ -192,24 +205,39 @@ def test_split_count_forced_and_sized(monkeypatch):
     fits = [R for R in (64, 128, 256, 512)
             if n3 == spans + a256(2 * vt * R * 128 * 4) + a256(2 * vt * R * 4)]
     assert len(fits) == 1 and n3 > n1
-    monkeypatch.setenv("HN_ATTN_SPLITS", "99")  # out of range: automatic choice
-    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None) == n1
+    # out-of-range options are an error, not a silent fallback
+    assert ws_size(c, s, n_splits=17) == 0 and "split counts" in hn.hn_last_error()
+    assert ws_size(c, s, n_splits_text=-1) == 0
+    assert ws_size(c, s, tile_rows=64) == 0 and "tile_rows" in hn.hn_last_error()
+    bad = hn.PlanOpts()
+    bad.reserved0 = 1
+    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None, ctypes.byref(bad)) == 0
+    sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
+    assert ws_size(c, s, sp, tile_rows=128) > 0
+    assert ws_size(c, s, sp, tile_rows=fits[0]) == (0 if fits[0] != 128 else ws_size(c, s, sp))
 
 
-def test_automatic_split_only_for_small_grids(monkeypatch):
+def test_tile_rows_option():
+    """tile_rows = 128 gives 128-row tiles to a dense plan (the default is the
+    kernel's larger tile); the plan records the height it was built with."""
+    c = fake_cache()
+    s = hn.SegLayout(0, 30, 24, 16, [8, 8], [0, 15], [15, 30])   # 720 video rows
+    n_auto, n_128 = ws_size(c, s), ws_size(c, s, tile_rows=128)
+    assert n_auto > 0 and n_128 > 0 and n_auto != n_128
+
+
+def test_automatic_split_only_for_small_grids():
     """Without a device (256 compute units assumed) a 16-head grid with short
     key lists is not split; a 1-head layout with 2 query tiles of long key
     lists is split to about two blocks per CU, capped at 16 and at 1024 keys
     per split."""
-    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
-    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "1")   # video tiles only here
     plan_sizes = {}
     for H, P, frames, W_ in ((16, 390, 30, 1), (1, 128, 2, 200)):
         c = fake_cache(H=H, P=P, W=W_)
         c.frames_seen = W_          # a full ring of history
         seg = hn.SegLayout(0, frames, P, 16, [], [], [])
         c.segments = 0
-        plan_sizes[H] = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+        plan_sizes[H] = ws_size(c, seg, n_splits_text=1)   # video tiles only here
     # 16 heads x 92 (or 46) tiles: spans only (no partial results)
     sizes = [-(-(-(-n_vt * 4 // 256) * 256 + n_vt * 4 * 32) // 256) * 256 for n_vt in (92 + 1, 46 + 1)]
     assert plan_sizes[16] in sizes
@@ -223,25 +251,20 @@ def test_automatic_split_only_for_small_grids(monkeypatch):
     assert any(ok)
 
 
-def test_automatic_two_splits_fill_the_last_round(monkeypatch):
+def test_automatic_two_splits_fill_the_last_round():
     """Without a device (256 compute units assumed): a 16-head grid whose last
     round of blocks is half empty and whose query tiles visit >= 16,384 keys
     (the 1280x704 steady state: 26,400 queries, 18-frame ring) is split in
     two; the same grid with short key lists (the 480x832 segment), and the
     2-head share (one round of blocks), are not.  The automatic workspace size
     must equal the one of the forced split count."""
-    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "1")
 
-    def ws(H, P, frames, W_, splits=None):
-        if splits is None:
-            monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
-        else:
-            monkeypatch.setenv("HN_ATTN_SPLITS", str(splits))
+    def ws(H, P, frames, W_, splits=0):
         c = fake_cache(H=H, P=P, W=W_)
         c.frames_seen = W_          # a full ring of history
         c.segments = 0
         seg = hn.SegLayout(0, frames, P, 16, [], [], [])
-        return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+        return ws_size(c, seg, n_splits=splits, n_splits_text=1)
 
     steady = (16, 880, 30, 18)       # 1,664 blocks of 256 rows: 6.5 rounds
     assert ws(*steady) == ws(*steady, splits=2) != ws(*steady, splits=1)
@@ -251,25 +274,20 @@ def test_automatic_two_splits_fill_the_last_round(monkeypatch):
     assert ws(*share) == ws(*share, splits=1)
 
 
-def test_text_split_count_follows_the_round_model(monkeypatch):
+def test_text_split_count_follows_the_round_model():
     """Without a device (256 compute units assumed): the text tiles of a joint
     launch are split so that they fill what the video blocks leave free.  The
     480x832 segment (736 unsplit video blocks: 32 slots free in the last
     round) takes 4; the 1280x704 steady state (video split in two: 13 full
     rounds) takes 8; short text tiles stay whole.  The automatic workspace
     size must equal the one of the forced count."""
-    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
 
-    def ws(H, P, frames, W_, text_splits=None, head=768, tails=(128,) * 4):
-        if text_splits is None:
-            monkeypatch.delenv("HN_ATTN_TEXT_SPLITS", raising=False)
-        else:
-            monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", str(text_splits))
+    def ws(H, P, frames, W_, text_splits=0, head=768, tails=(128,) * 4):
         c = fake_cache(H=H, P=P, W=W_, cap=4096)
         c.frames_seen = W_ if W_ > 1 else 0   # a full ring of history (none for the first segment)
         c.segments = 0
         seg = hn.SegLayout(0, frames, P, head, list(tails), [0] * len(tails), [frames] * len(tails))
-        return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c), None)
+        return ws_size(c, seg, n_splits_text=text_splits)
 
     first = (16, 390, 30, 1)
     assert ws(*first) == ws(*first, text_splits=4) != ws(*first, text_splits=8)
@@ -348,15 +366,13 @@ def test_attention_rejects_sources_over_2gib():
         raise AssertionError("no plan height accepted")
 
 
-def test_text_tiles_split_separately(monkeypatch):
+def test_text_tiles_split_separately():
     """Text query tiles get their own split count: forced to 4 with video tiles
     unsplit, the partial results cover only the text tiles."""
-    monkeypatch.delenv("HN_ATTN_SPLITS", raising=False)
     c = fake_cache()
     s = seg_c()
-    n1 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
-    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "4")
-    n4 = hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None)
+    n1 = ws_size(c, s)
+    n4 = ws_size(c, s, n_splits_text=4)
     a256 = lambda b: -(-b // 256) * 256
     vt = 1 + 4                                 # video tile unsplit + text tile x 4
     spans = a256(a256(vt * 4) + vt * 6 * 32)

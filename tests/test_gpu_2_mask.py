@@ -27,14 +27,13 @@ def data_of(name):
                                            ("c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4",
                                             "c2", "c3", "c4", "c5")] +
                          [(n, "128") for n in ("c1", "m1", "m2", "m4", "c2")])
-def test_dense_mask_matches_oracle(name, rows_env, monkeypatch):
+def test_dense_mask_matches_oracle(name, rows_env):
     # the spans are built per plan tile; both tile heights must expand to the oracle mask
     print(f"[mask] {name} rows={rows_env}", flush=True)
-    if rows_env != "auto":
-        monkeypatch.setenv("HN_ATTN_DENSE_ROWS", rows_env)
+    opts = None if rows_env == "auto" else hn.PlanOpts(tile_rows=int(rows_env))
     w = W.config(name)
     d = data_of(name)
-    run = G.Run(w, d)
+    run = G.Run(w, d, opts=opts)
     nq = w.current.video_len
     rows = np.arange(nq) if nq <= 2048 else G.sample_rows(nq)
     csr = d.get("csr") if w.sparse_keep is not None else None

@@ -51,14 +51,13 @@ def _compare(w, d, run, rows, kv=None):
 
 @pytest.mark.parametrize("rows", ["auto", "128"])
 @pytest.mark.parametrize("name", ["c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4"])
-def test_attention_small_all_rows(name, rows, monkeypatch):
+def test_attention_small_all_rows(name, rows):
     # dense plans use 256-row blocks; "128" forces the 128-row blocks (4 waves)
     print(f"[attn] {name} rows={rows}", flush=True)
-    if rows != "auto":
-        monkeypatch.setenv("HN_ATTN_DENSE_ROWS", rows)
+    opts = None if rows == "auto" else hn.PlanOpts(tile_rows=int(rows))
     w = W.config(name)
     d = data_of(name)
-    run = G.Run(w, d)
+    run = G.Run(w, d, opts=opts)
     if rows != "auto" and w.sparse_keep is None:
         assert run.plan.c.tile_q == int(rows)
     _compare(w, d, run, np.arange(w.current.video_len))

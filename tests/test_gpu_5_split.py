@@ -1,7 +1,7 @@
 """GPU parity of split-KV (key ranges of a query tile run as separate blocks,
 partial results merged; one softmax over the union of keys).
 
-The split count is forced through HN_ATTN_SPLITS on layouts with masks,
+The split count is forced through the plan options on layouts with masks,
 ragged tiles, history, keep lists and text queries, and on the head-share
 layout c3_h2 (2 heads of the 1280x704 steady state); more splits than 64-key
 blocks leave some splits empty.  (The automatic choice is host logic, tested
@@ -18,6 +18,7 @@ import workloads as W
 pytestmark = pytest.mark.gpu
 
 if torch.cuda.is_available():
+    import masked_attention_hn_amd as hn
     import _gpu as G
 
 _DATA = {}
@@ -36,13 +37,11 @@ def _bar(w, got, ref):
 @pytest.mark.parametrize("name,splits,text_splits", [("c1", 3, 1), ("c1", 16, 16), ("c1_evict", 2, 3),
                                                      ("m1", 5, 1), ("m1", 1, 4), ("m2", 4, 2),
                                                      ("m3", 3, 1), ("m4", 7, 5), ("m4", 1, 3)])
-def test_forced_splits(name, splits, text_splits, monkeypatch):
+def test_forced_splits(name, splits, text_splits):
     print(f"[split] {name} x{splits} text x{text_splits}", flush=True)
-    monkeypatch.setenv("HN_ATTN_SPLITS", str(splits))
-    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", str(text_splits))
     w = W.config(name)
     d = data_of(name)
-    run = G.Run(w, d)
+    run = G.Run(w, d, opts=hn.PlanOpts(n_splits=splits, n_splits_text=text_splits))
     assert run.plan.c.n_splits == splits and run.plan.c.n_splits_text == text_splits
     if w.current.text_len > 0:
         o, o_txt, lse, lse_txt = run.attn_joint()
@@ -68,12 +67,7 @@ def test_head_share_forced_split():
     print("[split] c3_h2 x6", flush=True)
     w = W.config("c3_h2")
     d = data_of("c3_h2")
-    import os
-    os.environ["HN_ATTN_SPLITS"] = "6"
-    try:
-        run = G.Run(w, d)
-    finally:
-        del os.environ["HN_ATTN_SPLITS"]
+    run = G.Run(w, d, opts=hn.PlanOpts(n_splits=6))
     assert run.plan.c.n_splits == 6
     o, lse = run.attn()
     rows = G.sample_rows(w.current.video_len)
@@ -83,13 +77,11 @@ def test_head_share_forced_split():
     assert np.abs(lse.cpu().numpy()[:, rows] - ref_lse).max() <= 1e-2
 
 
-def test_split_joint_deterministic_bitwise(monkeypatch):
+def test_split_joint_deterministic_bitwise():
     """A joint launch with video and text tiles split (partials merged) gives
     bit-identical outputs on repeated calls with the same plan."""
-    monkeypatch.setenv("HN_ATTN_SPLITS", "4")
-    monkeypatch.setenv("HN_ATTN_TEXT_SPLITS", "3")
     w = W.config("m1")
-    run = G.Run(w, data_of("m1"))
+    run = G.Run(w, data_of("m1"), opts=hn.PlanOpts(n_splits=4, n_splits_text=3))
     first = [t.clone() for t in run.attn_joint()]
     for _ in range(3):
         for a, b in zip(run.attn_joint(), first):
