@@ -372,6 +372,35 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* cache, const hn_seg_layout* seg,
                           void* o_vid, void* o_txt, float* lse, float* lse_txt,
                           float sm_scale, hipStream_t stream);
 
+/* Bytes of the library's own plan buffer for hn_seg_attn_fwd_noalloc: one
+ * per GPU the library runs on, held until the process ends. */
+#define HN_NOALLOC_PLAN_BYTES (4u << 20)
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation: the tile
+ * plan (hn_attn_mask_build, TILE_PLAN mode) and the attention
+ * (hn_seg_attn_fwd) in one call, with the plan written to a device buffer of
+ * the library's own (HN_NOALLOC_PLAN_BYTES per GPU, a static array) instead
+ * of a caller workspace.  Nothing is allocated: the buffer's address on the
+ * current device is looked up once, on the first call on that device.  Its
+ * plans never split keys (split-KV partial results would need far more
+ * memory), so the outputs equal, bit for bit, those of hn_seg_attn_fwd with a
+ * plan built with opts n_splits = n_splits_text = 1.
+ * Arguments: as hn_seg_attn_fwd, with `sparse` (nullable) as in
+ * hn_attn_mask_build.  Every call on one GPU shares that GPU's buffer and
+ * leaves its plan there: calls that overlap in time on one GPU (streams not
+ * ordered against each other) race; serialise them.
+ * Errors: as hn_seg_attn_fwd and hn_attn_mask_build; HN_ERR_WORKSPACE if the
+ * plan needs more than HN_NOALLOC_PLAN_BYTES (keep lists of very long
+ * segments); HN_ERR_HIP if the buffer's address cannot be obtained.  All are
+ * returned before anything is enqueued.
+ */
+hn_status hn_seg_attn_fwd_noalloc(const hn_kv_cache* cache, const hn_seg_layout* seg,
+                                  const hn_block_sparse* sparse, const void* q_vid, const void* q_txt,
+                                  const void* k_txt, const void* v_txt, const void* k_vid,
+                                  const void* v_vid, void* o_vid, void* o_txt, float* lse,
+                                  float* lse_txt, float sm_scale, hipStream_t stream);
+
 /* Camera cross-attention of the current segment's video tokens.
  *
  * Each latent frame carries one camera token (four consecutive frame poses

@@ -10,7 +10,7 @@ The exported functions carry the C names:
     hn_kv_quant_append, hn_attn_mask_build, hn_seg_attn_fwd,
     hn_attn_workspace_size, hn_kv_cache_sizes, hn_kv_cache_reset,
     hn_kv_archive_evict, hn_kv_cache_rewind, hn_camera_attn_fwd,
-    hn_status_string, hn_last_error
+    hn_seg_attn_fwd_noalloc, hn_status_string, hn_last_error
 plus small helpers (KVCache, KVArchive, SegLayout, BlockSparse, PlanOpts,
 build_plan, dense_mask, seg_attn, seg_attn_joint) that own the buffers those
 calls need.
@@ -117,6 +117,15 @@ _lib.hn_seg_attn_fwd.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_
                                  ctypes.c_float, _vp]
 _lib.hn_seg_attn_fwd.restype = _S
 
+_lib.hn_seg_attn_fwd_noalloc.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
+                                         ctypes.POINTER(hn_block_sparse),
+                                         _vp, _vp,            # q_vid, q_txt
+                                         _vp, _vp, _vp, _vp,  # k_txt, v_txt, k_vid, v_vid
+                                         _vp, _vp, _vp, _vp,  # o_vid, o_txt, lse, lse_txt
+                                         ctypes.c_float, _vp]
+_lib.hn_seg_attn_fwd_noalloc.restype = _S
+NOALLOC_PLAN_BYTES = 4 << 20
+
 _lib.hn_kv_archive_evict.argtypes = [ctypes.POINTER(hn_kv_cache), ctypes.POINTER(hn_seg_layout),
                                      ctypes.POINTER(hn_kv_archive), _vp]
 _lib.hn_kv_archive_evict.restype = _S
@@ -130,7 +139,7 @@ _lib.hn_camera_attn_fwd.restype = _S
 
 EXPORTS = ["hn_status_string", "hn_last_error", "hn_kv_cache_sizes", "hn_kv_cache_reset",
            "hn_kv_quant_append", "hn_attn_workspace_size", "hn_attn_mask_build", "hn_seg_attn_fwd",
-           "hn_kv_archive_evict", "hn_kv_cache_rewind", "hn_camera_attn_fwd"]
+           "hn_kv_archive_evict", "hn_kv_cache_rewind", "hn_camera_attn_fwd", "hn_seg_attn_fwd_noalloc"]
 
 
 class HNError(RuntimeError):
@@ -420,6 +429,20 @@ def seg_attn_joint(cache: KVCache, seg: SegLayout, plan: Plan, q_vid, q_txt, k_t
     hn_seg_attn_fwd(cache, seg, plan, q_vid, k_txt, v_txt, k_vid, v_vid, o, lse, sm_scale, stream,
                     q_txt=q_txt, o_txt=o_txt, lse_txt=lse_txt)
     return o, o_txt, lse, lse_txt
+
+
+def hn_seg_attn_fwd_noalloc(cache: KVCache, seg: SegLayout, sparse: Optional[BlockSparse], q_vid, k_txt,
+                            v_txt, k_vid, v_vid, o_vid: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                            sm_scale: Optional[float] = None, stream=None, q_txt=None,
+                            o_txt: Optional[torch.Tensor] = None, lse_txt: Optional[torch.Tensor] = None):
+    """Plan and attention in one call, with the plan in the library's own
+    device buffer (no workspace; for callers that cannot allocate)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(HEAD_DIM)
+    _check(_lib.hn_seg_attn_fwd_noalloc(ctypes.byref(cache.c), ctypes.byref(seg.c), _sp(sparse),
+                                        _ptr(q_vid), _ptr(q_txt), _ptr(k_txt), _ptr(v_txt), _ptr(k_vid),
+                                        _ptr(v_vid), _ptr(o_vid), _ptr(o_txt), _ptr(lse), _ptr(lse_txt),
+                                        float(sm_scale), _stream(stream)))
 
 
 def hn_camera_attn_fwd(seg: SegLayout, num_heads: int, radius: int, q_vid, k_cam, v_cam,

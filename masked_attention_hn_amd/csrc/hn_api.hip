@@ -11,10 +11,17 @@
 #include <cstdlib>
 #include <cstring>
 
+#include <mutex>
 #include <queue>
 #include <vector>
 
 #include "hn_internal.h"
+
+// The plan buffer of hn_seg_attn_fwd_noalloc.  Each GPU the library runs on
+// holds its own copy, at its own address, until the process ends.  In host
+// code this name is only a handle for hipGetSymbolAddress: kernels, copies and
+// fills take the per-device address that call returns (scratch_address below).
+static __device__ __align__(256) unsigned char scratch[HN_NOALLOC_PLAN_BYTES];
 
 namespace {
 
@@ -349,6 +356,183 @@ hn_status archive_copy(const hn_kv_cache* c, const hn_kv_archive* a, int64_t g0,
   return HN_OK;
 }
 
+// The host description of a plan built from pp into the device buffer dev.
+void fill_plan(const hn::PlanParams& pp, const hn_kv_cache* c, const hn_seg_layout* s, void* dev,
+               hn_tile_plan* plan) {
+  plan->dev = dev;
+  plan->tile_q = pp.tile_q;
+  plan->n_qtiles = pp.n_qtiles;
+  plan->n_text_tiles = pp.n_text_tiles;
+  plan->max_spans = pp.max_spans;
+  plan->seg_index = s->index;
+  plan->head_tokens = c->head_tokens;
+  plan->frames_seen = c->frames_seen;
+  plan->sparse = pp.sparse;
+  plan->n_splits = pp.n_splits;
+  plan->n_splits_text = pp.n_splits_text;
+  plan->reserved0 = 0;
+  {
+    // text queries: every text row sees heads, ring, own head and own
+    // video; a tail row also sees its own tail
+    const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
+    int64_t pairs = (int64_t)pp.text_len * base;
+    for (int j = 0; j < s->num_actions; ++j) pairs += (int64_t)s->action_len[j] * s->action_len[j];
+    plan->visible_pairs_text = pairs;
+  }
+  if (pp.sparse) {
+    plan->visible_pairs = -1;
+  } else {
+    int64_t pairs = 0;
+    const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
+    for (int f = 0; f < s->frames; ++f) {
+      int64_t n = base;
+      for (int j = 0; j < s->num_actions; ++j)
+        if (s->action_f0[j] <= f && f < s->action_f1[j]) n += s->action_len[j];
+      pairs += n * pp.P;
+    }
+    plan->visible_pairs = pairs;
+  }
+}
+
+// Per-device address of `scratch`, looked up on the first call on each
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+hn_status scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(HN_ERR_UNSUPPORTED, "device %d: the no-allocation path keeps %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress of the plan buffer");
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return HN_OK;
+}
+
+// Every check of an attention call and its kernel parameters; enqueues
+// nothing.  *partials says whether some launched tile is split (merge needed).
+hn_status attn_prepare(const hn_kv_cache* c, const hn_seg_layout* s, const hn_tile_plan* plan,
+                       const void* q_vid, const void* q_txt, const void* k_txt, const void* v_txt,
+                       const void* k_vid, const void* v_vid, void* o_vid, void* o_txt, float* lse,
+                       float* lse_txt, float sm_scale, hn::AttnParams* out, hn::MergeParams* merge,
+                       bool* partials_out) {
+  hn_status st = check_cache(c);
+  if (st != HN_OK) return st;
+  int64_t tl = 0;
+  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
+  if (!plan || !plan->dev) return fail(HN_ERR_NULL, "plan is NULL");
+  if (s->index != c->segments)
+    return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
+  const int P = c->tokens_per_frame;
+  const int lq = s->frames * P;
+  const int tq = plan->tile_q;
+  if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
+      plan->head_tokens != c->head_tokens || !valid_tile_rows(tq, plan->sparse != 0) ||
+      plan->n_qtiles != (int)ceil_div(lq, tq) || plan->n_text_tiles != (int)ceil_div(tl, tq) ||
+      plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS || plan->n_splits_text < 1 ||
+      plan->n_splits_text > HN_MAX_SPLITS)
+    return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
+  if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
+  if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
+  const bool text_q = q_txt != nullptr && tl > 0;
+  if (text_q && !o_txt) return fail(HN_ERR_NULL, "o_txt is NULL while q_txt is given");
+  // the kernel takes a tile's max over raw scores, valid for a positive scale
+  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
+    return fail(HN_ERR_INVALID, "sm_scale %g is not a positive finite number", (double)sm_scale);
+  // the kernel addresses every source through 32-bit buffer offsets
+  const int64_t tok_bytes = (int64_t)c->num_heads * HN_HEAD_DIM * 2;
+  const int64_t lim = INT_MAX;
+  if ((int64_t)lq * tok_bytes > lim || tl * tok_bytes > lim ||
+      (int64_t)c->head_cap_tokens * HN_HEAD_DIM > lim ||
+      (int64_t)c->window_frames * P * HN_HEAD_DIM > lim)
+    return fail(HN_ERR_UNSUPPORTED, "a key/value source exceeds 2 GiB");
+  hn::AttnParams p;
+  std::memset(&p, 0, sizeof(p));
+  p.H = c->num_heads;
+  p.lq = lq;
+  p.lq_txt = (int32_t)tl;
+  p.n_qtiles = plan->n_qtiles;
+  p.n_splits = plan->n_splits;
+  p.n_splits_text = plan->n_splits_text;
+  p.n_vt = hn::vt_count(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text);
+  p.n_tiles = hn::vt_count(plan->n_qtiles, text_q ? plan->n_text_tiles : 0, plan->n_splits, plan->n_splits_text);
+  // partial results exist iff some launched tile is split
+  const bool partials = plan->n_splits > 1 || (text_q && plan->n_splits_text > 1);
+  plan_partials(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text, &p.part_vt0,
+                &p.n_pvt);
+  p.tile_rows = plan->tile_q;
+  p.max_spans = plan->max_spans;
+  p.n_tasks = p.H * p.n_tiles;
+  p.tasks_per_xcd = (p.n_tasks + 7) / 8;
+  p.head_cap = c->head_cap_tokens;
+  p.ring_cap = c->window_frames * P;
+  p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.txt_len = (int32_t)tl;
+  p.has_i8 = (c->head_tokens > 0 || kept_frames(c) > 0) ? 1 : 0;
+  p.counts = static_cast<const int32_t*>(plan->dev);
+  p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
+                                              hn::plan_counts_bytes(p.n_vt));
+  if (p.n_pvt > 0) {
+    char* base = const_cast<char*>(static_cast<const char*>(plan->dev)) +
+                 hn::align256(hn::plan_spans_bytes(p.n_vt, plan->max_spans));
+    p.part_o = reinterpret_cast<float*>(base);
+    p.part_lse = reinterpret_cast<float*>(base + hn::plan_partial_o_bytes(p.H, p.n_pvt, plan->tile_q));
+  }
+  p.q = static_cast<const __bf16*>(q_vid);
+  p.q_txt = text_q ? static_cast<const __bf16*>(q_txt) : nullptr;
+  p.k_txt = static_cast<const __bf16*>(k_txt);
+  p.v_txt = static_cast<const __bf16*>(v_txt);
+  p.k_vid = static_cast<const __bf16*>(k_vid);
+  p.v_vid = static_cast<const __bf16*>(v_vid);
+  p.heads_k = c->heads_k; p.heads_v = c->heads_v; p.heads_ks = c->heads_ks; p.heads_vs = c->heads_vs;
+  p.ring_k = c->ring_k; p.ring_v = c->ring_v; p.ring_ks = c->ring_ks; p.ring_vs = c->ring_vs;
+  p.o = static_cast<__bf16*>(o_vid);
+  p.o_txt = text_q ? static_cast<__bf16*>(o_txt) : nullptr;
+  p.lse = lse;
+  p.lse_txt = text_q ? lse_txt : nullptr;
+  *out = p;
+  *partials_out = partials;
+  if (partials) {
+    hn::MergeParams& m = *merge;
+    std::memset(&m, 0, sizeof(m));
+    m.H = p.H;
+    m.n_splits = p.n_splits;
+    m.n_splits_text = p.n_splits_text;
+    m.part_vt0 = p.part_vt0;
+    m.n_pvt = p.n_pvt;
+    m.tile_rows = plan->tile_q;
+    m.n_qtiles = plan->n_qtiles;
+    m.n_tiles = plan->n_qtiles + (text_q ? plan->n_text_tiles : 0);
+    m.lq = lq;
+    m.lq_txt = (int32_t)tl;
+    m.part_o = p.part_o;
+    m.part_lse = p.part_lse;
+    m.o = p.o;
+    m.o_txt = p.o_txt;
+    m.lse = p.lse;
+    m.lse_txt = p.lse_txt;
+  }
+  return HN_OK;
+}
+
+hn_status attn_launch(const hn::AttnParams& p, const hn::MergeParams& m, bool partials, hipStream_t stream) {
+  hipError_t e = hn::launch_attn(p, stream);
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  if (partials) {
+    e = hn::launch_merge(m, stream);
+    if (e != hipSuccess) return hip_fail(e, "split merge launch");
+  }
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -511,39 +695,7 @@ hn_status hn_attn_mask_build(const hn_kv_cache* c, const hn_seg_layout* s, const
       return fail(HN_ERR_WORKSPACE, "workspace of %zu bytes; %zu needed", out_bytes, need);
     hipError_t e = hn::launch_plan(pp, out, stream);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
-    plan->dev = out;
-    plan->tile_q = pp.tile_q;
-    plan->n_qtiles = pp.n_qtiles;
-    plan->n_text_tiles = pp.n_text_tiles;
-    plan->max_spans = pp.max_spans;
-    plan->seg_index = s->index;
-    plan->head_tokens = c->head_tokens;
-    plan->frames_seen = c->frames_seen;
-    plan->sparse = pp.sparse;
-    plan->n_splits = pp.n_splits;
-    plan->n_splits_text = pp.n_splits_text;
-    plan->reserved0 = 0;
-    {
-      // text queries: every text row sees heads, ring, own head and own
-      // video; a tail row also sees its own tail
-      const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
-      int64_t pairs = (int64_t)pp.text_len * base;
-      for (int j = 0; j < s->num_actions; ++j) pairs += (int64_t)s->action_len[j] * s->action_len[j];
-      plan->visible_pairs_text = pairs;
-    }
-    if (pp.sparse) {
-      plan->visible_pairs = -1;
-    } else {
-      int64_t pairs = 0;
-      const int64_t base = (int64_t)pp.head_tokens + pp.ring_tokens + s->head_len + pp.lq;
-      for (int f = 0; f < s->frames; ++f) {
-        int64_t n = base;
-        for (int j = 0; j < s->num_actions; ++j)
-          if (s->action_f0[j] <= f && f < s->action_f1[j]) n += s->action_len[j];
-        pairs += n * pp.P;
-      }
-      plan->visible_pairs = pairs;
-    }
+    fill_plan(pp, c, s, out, plan);
     return ok();
   }
   if (mode != HN_MASK_DENSE) return fail(HN_ERR_INVALID, "unknown mask mode %d", (int)mode);
@@ -573,105 +725,48 @@ hn_status hn_seg_attn_fwd(const hn_kv_cache* c, const hn_seg_layout* s, const hn
                           const void* q_vid, const void* q_txt, const void* k_txt, const void* v_txt,
                           const void* k_vid, const void* v_vid, void* o_vid, void* o_txt, float* lse,
                           float* lse_txt, float sm_scale, hipStream_t stream) {
-  hn_status st = check_cache(c);
-  if (st != HN_OK) return st;
-  int64_t tl = 0;
-  if ((st = check_seg(c, s, &tl)) != HN_OK) return st;
-  if (!plan || !plan->dev) return fail(HN_ERR_NULL, "plan is NULL");
-  if (s->index != c->segments)
-    return fail(HN_ERR_ORDER, "segment index %d but the cache holds %d segments", s->index, c->segments);
-  const int P = c->tokens_per_frame;
-  const int lq = s->frames * P;
-  const int tq = plan->tile_q;
-  if (plan->seg_index != s->index || plan->frames_seen != c->frames_seen ||
-      plan->head_tokens != c->head_tokens || !valid_tile_rows(tq, plan->sparse != 0) ||
-      plan->n_qtiles != (int)ceil_div(lq, tq) || plan->n_text_tiles != (int)ceil_div(tl, tq) ||
-      plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS || plan->n_splits_text < 1 ||
-      plan->n_splits_text > HN_MAX_SPLITS)
-    return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
-  if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
-  if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
-  const bool text_q = q_txt != nullptr && tl > 0;
-  if (text_q && !o_txt) return fail(HN_ERR_NULL, "o_txt is NULL while q_txt is given");
-  // the kernel takes a tile's max over raw scores, valid for a positive scale
-  if (!std::isfinite(sm_scale) || !(sm_scale > 0.0f))
-    return fail(HN_ERR_INVALID, "sm_scale %g is not a positive finite number", (double)sm_scale);
-  // the kernel addresses every source through 32-bit buffer offsets
-  const int64_t tok_bytes = (int64_t)c->num_heads * HN_HEAD_DIM * 2;
-  const int64_t lim = INT_MAX;
-  if ((int64_t)lq * tok_bytes > lim || tl * tok_bytes > lim ||
-      (int64_t)c->head_cap_tokens * HN_HEAD_DIM > lim ||
-      (int64_t)c->window_frames * P * HN_HEAD_DIM > lim)
-    return fail(HN_ERR_UNSUPPORTED, "a key/value source exceeds 2 GiB");
   hn::AttnParams p;
-  std::memset(&p, 0, sizeof(p));
-  p.H = c->num_heads;
-  p.lq = lq;
-  p.lq_txt = (int32_t)tl;
-  p.n_qtiles = plan->n_qtiles;
-  p.n_splits = plan->n_splits;
-  p.n_splits_text = plan->n_splits_text;
-  p.n_vt = hn::vt_count(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text);
-  p.n_tiles = hn::vt_count(plan->n_qtiles, text_q ? plan->n_text_tiles : 0, plan->n_splits, plan->n_splits_text);
-  // partial results exist iff some launched tile is split
-  const bool partials = plan->n_splits > 1 || (text_q && plan->n_splits_text > 1);
-  plan_partials(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text, &p.part_vt0,
-                &p.n_pvt);
-  p.tile_rows = plan->tile_q;
-  p.max_spans = plan->max_spans;
-  p.n_tasks = p.H * p.n_tiles;
-  p.tasks_per_xcd = (p.n_tasks + 7) / 8;
-  p.head_cap = c->head_cap_tokens;
-  p.ring_cap = c->window_frames * P;
-  p.scale_log2 = sm_scale * 1.4426950408889634f;
-  p.txt_len = (int32_t)tl;
-  p.has_i8 = (c->head_tokens > 0 || kept_frames(c) > 0) ? 1 : 0;
-  p.counts = static_cast<const int32_t*>(plan->dev);
-  p.spans = reinterpret_cast<const hn::Span*>(static_cast<const char*>(plan->dev) +
-                                              hn::plan_counts_bytes(p.n_vt));
-  if (p.n_pvt > 0) {
-    char* base = const_cast<char*>(static_cast<const char*>(plan->dev)) +
-                 hn::align256(hn::plan_spans_bytes(p.n_vt, plan->max_spans));
-    p.part_o = reinterpret_cast<float*>(base);
-    p.part_lse = reinterpret_cast<float*>(base + hn::plan_partial_o_bytes(p.H, p.n_pvt, plan->tile_q));
-  }
-  p.q = static_cast<const __bf16*>(q_vid);
-  p.q_txt = text_q ? static_cast<const __bf16*>(q_txt) : nullptr;
-  p.k_txt = static_cast<const __bf16*>(k_txt);
-  p.v_txt = static_cast<const __bf16*>(v_txt);
-  p.k_vid = static_cast<const __bf16*>(k_vid);
-  p.v_vid = static_cast<const __bf16*>(v_vid);
-  p.heads_k = c->heads_k; p.heads_v = c->heads_v; p.heads_ks = c->heads_ks; p.heads_vs = c->heads_vs;
-  p.ring_k = c->ring_k; p.ring_v = c->ring_v; p.ring_ks = c->ring_ks; p.ring_vs = c->ring_vs;
-  p.o = static_cast<__bf16*>(o_vid);
-  p.o_txt = text_q ? static_cast<__bf16*>(o_txt) : nullptr;
-  p.lse = lse;
-  p.lse_txt = text_q ? lse_txt : nullptr;
-  hipError_t e = hn::launch_attn(p, stream);
-  if (e != hipSuccess) return hip_fail(e, "attention launch");
-  if (partials) {
-    hn::MergeParams m;
-    std::memset(&m, 0, sizeof(m));
-    m.H = p.H;
-    m.n_splits = p.n_splits;
-    m.n_splits_text = p.n_splits_text;
-    m.part_vt0 = p.part_vt0;
-    m.n_pvt = p.n_pvt;
-    m.tile_rows = plan->tile_q;
-    m.n_qtiles = plan->n_qtiles;
-    m.n_tiles = plan->n_qtiles + (text_q ? plan->n_text_tiles : 0);
-    m.lq = lq;
-    m.lq_txt = (int32_t)tl;
-    m.part_o = p.part_o;
-    m.part_lse = p.part_lse;
-    m.o = p.o;
-    m.o_txt = p.o_txt;
-    m.lse = p.lse;
-    m.lse_txt = p.lse_txt;
-    e = hn::launch_merge(m, stream);
-    if (e != hipSuccess) return hip_fail(e, "split merge launch");
-  }
-  return ok();
+  hn::MergeParams m;
+  bool partials = false;
+  const hn_status st = attn_prepare(c, s, plan, q_vid, q_txt, k_txt, v_txt, k_vid, v_vid, o_vid, o_txt, lse,
+                                    lse_txt, sm_scale, &p, &m, &partials);
+  if (st != HN_OK) return st;
+  return attn_launch(p, m, partials, stream);
+}
+
+hn_status hn_seg_attn_fwd_noalloc(const hn_kv_cache* c, const hn_seg_layout* s, const hn_block_sparse* sp,
+                                  const void* q_vid, const void* q_txt, const void* k_txt, const void* v_txt,
+                                  const void* k_vid, const void* v_vid, void* o_vid, void* o_txt, float* lse,
+                                  float* lse_txt, float sm_scale, hipStream_t stream) {
+  // no key splits: the plan is counts and spans only (no partial results)
+  const hn_plan_opts unsplit = {1, 1, 0, 0};
+  hn::PlanParams pp;
+  hn_status st = make_plan_params(c, s, sp, &unsplit, &pp);
+  if (st != HN_OK) return st;
+  const size_t need = plan_ws_bytes(c, pp);
+  if (need > (size_t)HN_NOALLOC_PLAN_BYTES)
+    return fail(HN_ERR_WORKSPACE, "plan of %zu bytes exceeds the %zu-byte buffer of the no-allocation path", need,
+                (size_t)HN_NOALLOC_PLAN_BYTES);
+  // every argument check first (the plan's device address does not take part
+  // in them), then the buffer's address, then the same parameters with it
+  hn_tile_plan plan;
+  std::memset(&plan, 0, sizeof(plan));
+  fill_plan(pp, c, s, reinterpret_cast<void*>(alignof(hn::Span)), &plan);
+  hn::AttnParams p;
+  hn::MergeParams m;
+  bool partials = false;
+  st = attn_prepare(c, s, &plan, q_vid, q_txt, k_txt, v_txt, k_vid, v_vid, o_vid, o_txt, lse, lse_txt, sm_scale,
+                    &p, &m, &partials);
+  if (st != HN_OK) return st;
+  void* ws = nullptr;
+  if ((st = scratch_address(&ws)) != HN_OK) return st;
+  plan.dev = ws;
+  st = attn_prepare(c, s, &plan, q_vid, q_txt, k_txt, v_txt, k_vid, v_vid, o_vid, o_txt, lse, lse_txt, sm_scale,
+                    &p, &m, &partials);
+  if (st != HN_OK) return st;
+  const hipError_t e = hn::launch_plan(pp, ws, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  return attn_launch(p, m, partials, stream);
 }
 
 hn_status hn_camera_attn_fwd(const hn_seg_layout* s, int32_t num_heads, int32_t radius, const void* q_vid,
