@@ -40,7 +40,8 @@ def parse():
                     help="untimed steps; the clock ramps over the first ~50 ms of work")
     ap.add_argument("--workload", default="c2", help="c2 (default), c3, c4 or c5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=11700, help="query rows the oracle computes")
+    ap.add_argument("--cpu-rows", type=int, default=None,
+                    help="query rows the oracle computes (default: about 10-30 s of CPU work)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the joint, camera and archive measurements (counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -196,9 +197,6 @@ def main():
     saved = (cache.c.frames_seen, cache.c.head_tokens, cache.c.segments)
     pairs = visible_pairs(w, csr)
     flops = 4.0 * 128 * pairs * w.heads
-    surv_frames = min(w.current.frames, w.ring_frames)
-    append_rows = (w.current.head_len + surv_frames * w.current.tokens_per_frame) * w.heads
-    append_bytes = append_rows * APPEND_BYTES_PER_ROW
 
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -229,37 +227,74 @@ def main():
     if plan_c.visible_pairs >= 0:
         assert plan_c.visible_pairs == pairs, (plan_c.visible_pairs, pairs)
 
-    # quantize/append alone, rotating input and ring buffers (> 256 MB MALL)
-    n_sets = max(3, math.ceil(600e6 / max(1, append_bytes)))
-    sets = []
-    for r in range(n_sets):
-        c = hn.KVCache(w.heads, w.current.tokens_per_frame, w.ring_frames, max(1, w.current.head_len))
-        kv = [t.clone() for t in (k_txt, v_txt, k_vid, v_vid)]
-        sets.append((c, kv))
-    seg0 = lay(0, w.current)
-    for c, kv in sets:
-        hn.hn_kv_quant_append(c, seg0, *kv)
-        hn.hn_kv_cache_reset(c)
-    torch.cuda.synchronize()
-    reps = 4 * n_sets
-    e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        c, kv = sets[i % n_sets]
-        hn.hn_kv_cache_reset(c)
-        e0[i].record(stream)
-        hn.hn_kv_quant_append(c, seg0, *kv)
-        e1[i].record(stream)
-    torch.cuda.synchronize()
-    app_ms = sorted(a.elapsed_time(b) for a, b in zip(e0, e1))
-    app_med = app_ms[len(app_ms) // 2]
-    append_gbs = append_bytes / (app_med * 1e-3) / 1e9
+    def time_append(cur, kv, window, heads):
+        """Median time of the quantize/append kernel alone on segment shape
+        cur (appended as segment 0 into an empty cache with a window of
+        `window` frames), rotating input and cache buffers over > 600 MB (more
+        than the 256 MB MALL) so that every launch reads and writes HBM."""
+        surv = min(cur.frames, window)
+        nbytes = (cur.head_len + surv * cur.tokens_per_frame) * heads * APPEND_BYTES_PER_ROW
+        n_sets = max(3, math.ceil(600e6 / max(1, nbytes)))
+        sets = []
+        for r in range(n_sets):
+            c = hn.KVCache(heads, cur.tokens_per_frame, window, max(1, cur.head_len))
+            sets.append((c, [t.clone() for t in kv]))
+        seg0 = lay(0, cur)
+        for c, kvs in sets:
+            hn.hn_kv_quant_append(c, seg0, *kvs)
+            hn.hn_kv_cache_reset(c)
+        torch.cuda.synchronize()
+        reps = 4 * n_sets
+        e0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        e1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            c, kvs = sets[i % n_sets]
+            hn.hn_kv_cache_reset(c)
+            e0[i].record(stream)
+            hn.hn_kv_quant_append(c, seg0, *kvs)
+            e1[i].record(stream)
+        torch.cuda.synchronize()
+        del sets
+        ms = sorted(a.elapsed_time(b) for a, b in zip(e0, e1))[reps // 2]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {
+            "kernel": "quant_append_kernel",
+            "bound": "hbm",
+            "rows": (cur.head_len + surv * cur.tokens_per_frame) * heads,
+            "bytes": nbytes,
+            "median_ms": round(ms, 4),
+            "achieved": round(gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "rotating_sets": n_sets,
+        }
+
+    append = time_append(w.current, (k_txt, v_txt, k_vid, v_vid), w.ring_frames, w.heads)
+    append["shape"] = f"this workload's segment ({args.workload})"
+    # the 1280x704 segment with no window (30 frames x 880 tokens + 768-token
+    # head, 16 heads: 337 MB), seeded N(0,1) bf16 drawn on the device
+    big = W.config("c4").current
+    if w.heads == 16 and (w.current.frames, w.current.tokens_per_frame, w.current.head_len,
+                          w.ring_frames >= big.frames) == (big.frames, big.tokens_per_frame,
+                                                           big.head_len, True):
+        append_big = dict(append)
+    else:
+        g = torch.Generator(device=dev)
+        g.manual_seed(1280704)
+        mk = lambda n: torch.randn((n, 16, 128), generator=g, device=dev).to(torch.bfloat16)
+        kv_big = (mk(big.text_len), mk(big.text_len), mk(big.video_len), mk(big.video_len))
+        append_big = time_append(big, kv_big, big.frames, 16)
+        del kv_big
+    append_big["shape"] = "1280x704 segment, no window: (768 + 30 x 880) tokens x 16 heads"
 
     traffic = counter_traffic(args.workload)
 
-    # camera cross-attention (radius 0: each video token reads its own latent
-    # frame's camera token); rotating query/output sets over 600 MB so the
-    # bytes come from HBM
+    # camera cross-attention: each video token attends to the camera tokens of
+    # its segment within `radius` latent frames of its own.  Radius 0 reduces
+    # to a copy of the frame's camera value (one key, weight 1); radius 1 (up
+    # to 3 keys) exercises the scores and the softmax.  Rotating query/output
+    # sets over 600 MB so the bytes come from HBM.
     camera = None
     k_cam, v_cam = to_dev(data["k_cam"]), to_dev(data["v_cam"])
     cam_rows = w.current.video_len * w.heads
@@ -268,30 +303,39 @@ def main():
     cam_sets = [(q.clone(), torch.empty_like(q),
                  torch.empty((w.heads, w.current.video_len), dtype=torch.float32, device=dev))
                 for _ in range(n_cam)]
-    for qq, oo, ll in cam_sets:
-        hn.hn_camera_attn_fwd(seg, w.heads, 0, qq, k_cam, v_cam, oo, ll)
-    torch.cuda.synchronize()
-    reps = 4 * n_cam
-    ec0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ec1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        qq, oo, ll = cam_sets[i % n_cam]
-        ec0[i].record(stream)
-        hn.hn_camera_attn_fwd(seg, w.heads, 0, qq, k_cam, v_cam, oo, ll)
-        ec1[i].record(stream)
-    torch.cuda.synchronize()
-    cam_ms = sorted(a.elapsed_time(b) for a, b in zip(ec0, ec1))[reps // 2] if reps else 0.0
-    camera = None if not reps else {
-        "kernel": "camera_attn_kernel",
-        "what": "video tokens x heads reading their frame's camera token (radius 0)",
-        "bound": "hbm",
-        "bytes": cam_bytes,
-        "median_ms": round(cam_ms, 4),
-        "achieved": round(cam_bytes / (cam_ms * 1e-3) / 1e9, 1),
-        "peak": PEAK_HBM_GBS,
-        "unit": "GB/s",
-        "frac": round(cam_bytes / (cam_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-    }
+
+    def time_camera(radius):
+        for qq, oo, ll in cam_sets:
+            hn.hn_camera_attn_fwd(seg, w.heads, radius, qq, k_cam, v_cam, oo, ll)
+        torch.cuda.synchronize()
+        reps = 4 * n_cam
+        ec0 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        ec1 = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+        for i in range(reps):
+            qq, oo, ll = cam_sets[i % n_cam]
+            ec0[i].record(stream)
+            hn.hn_camera_attn_fwd(seg, w.heads, radius, qq, k_cam, v_cam, oo, ll)
+            ec1[i].record(stream)
+        torch.cuda.synchronize()
+        return sorted(a.elapsed_time(b) for a, b in zip(ec0, ec1))[reps // 2]
+
+    if n_cam:
+        cam_ms = time_camera(1)
+        cam0_ms = time_camera(0)
+        camera = {
+            "kernel": "camera_attn_kernel",
+            "what": "video tokens x heads attending to the camera tokens within 1 latent frame "
+                    "of their own (up to 3 keys; O, LSE written)",
+            "bound": "hbm",
+            "bytes": cam_bytes,
+            "median_ms": round(cam_ms, 4),
+            "achieved": round(cam_bytes / (cam_ms * 1e-3) / 1e9, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(cam_bytes / (cam_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+            "radius0_median_ms": round(cam0_ms, 4),
+            "radius0_achieved": round(cam_bytes / (cam0_ms * 1e-3) / 1e9, 1),
+        }
     del cam_sets
 
     # history archive: evict (device -> pinned host) the frames the append of
@@ -411,23 +455,15 @@ def main():
         "joint": joint,
         "archive": archive,
         "camera": camera,
-        "append": {
-            "kernel": "quant_append_kernel",
-            "bound": "hbm",
-            "bytes": append_bytes,
-            "median_ms": round(app_med, 4),
-            "achieved": round(append_gbs, 1),
-            "peak": PEAK_HBM_GBS,
-            "unit": "GB/s",
-            "frac": round(append_gbs / PEAK_HBM_GBS, 4),
-            "rotating_sets": n_sets,
-        },
+        "append": append,
+        "append_1280x704": append_big,
         "cpu_baseline": None,
     }
 
     if not args.no_cpu_baseline:
         import oracle
-        rows = np.linspace(0, w.current.video_len - 1, min(args.cpu_rows, w.current.video_len)).astype(int)
+        n_rows = args.cpu_rows or {"c3": 128, "c4": 64, "c3_h2": 1024}.get(args.workload, 11700)
+        rows = np.linspace(0, w.current.video_len - 1, min(n_rows, w.current.video_len)).astype(int)
         rows = np.unique(rows)
         tc0 = time.perf_counter()
         oracle.attention(w, data, rows)
@@ -438,21 +474,34 @@ def main():
         else:
             sample_pairs = pairs * len(rows) / w.current.video_len
         cpu_tflops = 4.0 * 128 * sample_pairs * w.heads / tc / 1e12
-        ncores = len(os.sched_getaffinity(0))
+        avail = len(os.sched_getaffinity(0))
+        threads = 1
         try:
             import threadpoolctl
             blas = [i["num_threads"] for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
             if blas:
-                ncores = min(ncores, max(blas))
+                threads = max(blas)
         except ImportError:
+            pass
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as fh:
+                for line in fh:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
             pass
         out["cpu_baseline"] = {
             "value": round(cpu_tflops, 6),
             "unit": "TFLOP/s",
-            "cores": ncores,
+            "cores": min(threads, avail),
             "kind": "oracle",
+            "cpu": cpu_model,
+            "cores_available": avail,
             "sample": f"{len(rows)} of {w.current.video_len} query rows (evenly spaced), all "
-                      f"{w.heads} heads, fp64 numpy oracle incl. key preparation; {tc:.1f} s",
+                      f"{w.heads} heads, fp64 numpy oracle incl. key preparation; {tc:.1f} s; "
+                      "its products run on the BLAS threads, the rest on one thread",
         }
     print(json.dumps(out), flush=True)
 
