@@ -1,9 +1,10 @@
 // INT8 quantize + ring append of one segment's keys and values (gfx950).
 //
-// Keys and values are stored INT8 with a float scale and computed in BF16
-// ("Hy-Nomas 拆解" teardown, section "单卡 4090 怎么做到的", first technique);
-// history video is a window of W latent frames, oldest evicted first (same
-// section, second technique).  Per (token, head) row of 128 values:
+// Keys and values are stored INT8 with a float scale and computed in 16-bit
+// floating point ("Hy-Nomas 拆解" teardown, section "单卡 4090 怎么做到的", first
+// technique); history video is a window of W latent frames, oldest evicted
+// first (same section, second technique).  Per (token, head) row of 128
+// values:
 //   scale = amax / 127 (IEEE fp32, correctly rounded),
 //   q     = round_half_even(x / scale) (correctly rounded fp32 quotient),
 //           clamped to [-127, 127]; a zero row stores scale 0 and q 0.
@@ -12,7 +13,12 @@
 // of K and 32 of V per lane), the row max is an 8-lane butterfly, and each
 // lane writes 16 int8 codes (one 16-byte store) per tensor.  Consecutive
 // 8-lane groups take the heads of one token, so each wave reads 8 x 256
-// contiguous bytes per tensor.  (16-byte stores measured 9-13% faster than
+// contiguous bytes per tensor and writes 8 rows of codes 8 heads apart (the
+// cache is head-major, so that an attention tile of 64 keys of one head is
+// one contiguous 8 KB block).  A token-major cache, whose writes are as
+// contiguous as the reads, made this kernel 2-10% faster but the INT8
+// attention tiles (64 rows 2 KB apart) 5-7% slower on 1280x704 segments with
+// history, which costs far more.  (16-byte stores measured 9-13% faster than
 // 8-byte ones; non-temporal loads/stores, two rows per lane group, and blocks
 // of 32 consecutive tokens of one head, which write their codes and scales
 // contiguously but read rows 4 KB apart, were slower: the last by 10%; so was
