@@ -3,7 +3,9 @@
 // One softmax over the union of visible keys of a video query
 // ("Hy-Nomas 拆解" teardown, section "架构": segment-causal plus action-aware
 // causal attention); history keys/values are INT8 with fp32 scales and the
-// arithmetic is BF16 (same page, "单卡 4090 怎么做到的", first technique).
+// arithmetic is 16-bit (same page, "单卡 4090 怎么做到的", first technique):
+// bf16 for the segment's own keys and values, fp16 for the dequantized
+// history (see "tile" below).
 //
 // Work decomposition (template <NW, QB, KT>)
 //   block  = one (head, query tile of 32*QB*NW rows); NW waves, each owning
