@@ -26,14 +26,15 @@
 //            INT8 tiles are read from HBM as int8 (half the bytes) with their
 //            per-token fp32 scales and dequantized in registers on their way
 //            into LDS, so the math never sees a scale.  They are staged and
-//            multiplied in fp16, not bf16: K' = fp16(code x scale) and
-//            V' = fp16(code x scale x 2^-7), against an fp16 copy of Q and
-//            fp16 probabilities that carry the 2^7 back.  fp16 keeps 11
-//            significant bits where bf16 keeps 8, which bounds the error of the
-//            dequantized history 8x tighter at the same MFMA rate; the
-//            power-of-two shifts keep K', V' and P inside fp16's range.  A tile
-//            whose scales would leave that range (|K| above 65,024 or |V| above
-//            8.3e6) falls back to bf16 K and V.
+//            multiplied in fp16, not bf16: K' = fp16(code x fp16(scale)) and
+//            V' = fp16(code x fp16(scale x 2^-7)), in packed fp16 arithmetic,
+//            against an fp16 copy of Q and fp16 probabilities that carry the
+//            2^7 back.  fp16 keeps 11 significant bits where bf16 keeps 8,
+//            which bounds the error of the dequantized history 4x tighter (two
+//            fp16 roundings against one bf16 rounding) at the same nominal
+//            MFMA rate; the power-of-two shifts keep K', V' and P inside
+//            fp16's range.  A tile whose scales would leave that range (|K|
+//            above 65,024 or |V| above 8.3e6) falls back to bf16 K and V.
 //   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then holds
 //            the tile's keys for one query, so the row max/sum are in-lane plus
 //            one v_permlane32_swap with lane^32); online softmax in the log2
@@ -143,42 +144,56 @@ __device__ inline void ld_lds16(rsrc_t r, void* dst, uint32_t voff, uint32_t sof
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, voff, soff, 0, 0);
 }
 
-// Four INT8 codes of w times the row scale sc -> two packed fp16 (F16) or
-// bf16 pairs.  With u = q + 128 (the codes' bytes xor 0x80), fma(u, sc,
-// -128 sc) is the correctly rounded fp32 product q * sc (128 sc is exact),
-// then rounded to the 16-bit type.
-template <bool F16>
-__device__ inline void i8x4_dequant(uint32_t w, float sc, float m128, uint32_t& p0, uint32_t& p1) {
+// Four INT8 codes of w times the row scale sc -> two packed bf16 pairs.
+// With u = q + 128 (the codes' bytes xor 0x80), fma(u, sc, -128 sc) is the
+// correctly rounded fp32 product q * sc (128 sc is exact), then rounded to
+// bf16.
+__device__ inline void i8x4_dequant_bf16(uint32_t w, float sc, float m128, uint32_t& p0, uint32_t& p1) {
   const uint32_t u = w ^ 0x80808080u;
   const float f0 = __builtin_fmaf((float)(u & 0xffu), sc, m128);
   const float f1 = __builtin_fmaf((float)((u >> 8) & 0xffu), sc, m128);
   const float f2 = __builtin_fmaf((float)((u >> 16) & 0xffu), sc, m128);
   const float f3 = __builtin_fmaf((float)(u >> 24), sc, m128);
-  if constexpr (F16) {
-    // keep the fp32 products apart from the conversion: fused into the
-    // mixed-precision FMA (fp32 inputs, fp16 result) the staging measured 2%
-    // slower on the history-dominated shapes
-    float g0 = f0, g1 = f1, g2 = f2, g3 = f3;
-    asm volatile("" : "+v"(g0), "+v"(g1), "+v"(g2), "+v"(g3));
-    const f16x2 a = {(_Float16)g0, (_Float16)g1};
-    const f16x2 b = {(_Float16)g2, (_Float16)g3};
-    p0 = __builtin_bit_cast(uint32_t, a);
-    p1 = __builtin_bit_cast(uint32_t, b);
-  } else {
-    const bf16x2 a = {(__bf16)f0, (__bf16)f1};
-    const bf16x2 b = {(__bf16)f2, (__bf16)f3};
-    p0 = __builtin_bit_cast(uint32_t, a);
-    p1 = __builtin_bit_cast(uint32_t, b);
-  }
+  const bf16x2 a = {(__bf16)f0, (__bf16)f1};
+  const bf16x2 b = {(__bf16)f2, (__bf16)f3};
+  p0 = __builtin_bit_cast(uint32_t, a);
+  p1 = __builtin_bit_cast(uint32_t, b);
 }
-// 16 INT8 codes of one row -> 16 dequantized 16-bit values (two 16-byte words).
+// Four INT8 codes of w times the fp16 row scale s2 -> two packed fp16 pairs,
+// in packed fp16 arithmetic: the byte u = q + 128 placed under the fp16
+// exponent of 1024 is the fp16 value 1024 + u (ulp 1 there), so one byte
+// permute makes two of them, one packed subtraction of 1152 gives q exactly,
+// and one packed multiply gives fp16(q x s2), rounded once.  (7 VALU
+// operations per 4 codes against 11 for the fp32 product and conversion.)
+__device__ inline void i8x4_dequant_f16(uint32_t w, f16x2 s2, uint32_t& p0, uint32_t& p1) {
+  const uint32_t u = w ^ 0x80808080u;
+  // bytes 4-7 of the permute's source are 0x64: codes 0, 1 -> halves of p0
+  const uint32_t e0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t e1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  const f16x2 q0 = __builtin_bit_cast(f16x2, e0) - bias;
+  const f16x2 q1 = __builtin_bit_cast(f16x2, e1) - bias;
+  p0 = __builtin_bit_cast(uint32_t, q0 * s2);
+  p1 = __builtin_bit_cast(uint32_t, q1 * s2);
+}
+// 16 INT8 codes of one row -> 16 dequantized 16-bit values (two 16-byte
+// words): fp16 (F16, scale rounded to fp16 first) or bf16.
 template <bool F16>
 __device__ inline void i8x16_dequant(uint4 w, float sc, uint4& lo, uint4& hi) {
-  const float m128 = -128.0f * sc;
-  i8x4_dequant<F16>(w.x, sc, m128, lo.x, lo.y);
-  i8x4_dequant<F16>(w.y, sc, m128, lo.z, lo.w);
-  i8x4_dequant<F16>(w.z, sc, m128, hi.x, hi.y);
-  i8x4_dequant<F16>(w.w, sc, m128, hi.z, hi.w);
+  if constexpr (F16) {
+    const _Float16 h = (_Float16)sc;
+    const f16x2 s2 = {h, h};
+    i8x4_dequant_f16(w.x, s2, lo.x, lo.y);
+    i8x4_dequant_f16(w.y, s2, lo.z, lo.w);
+    i8x4_dequant_f16(w.z, s2, hi.x, hi.y);
+    i8x4_dequant_f16(w.w, s2, hi.z, hi.w);
+  } else {
+    const float m128 = -128.0f * sc;
+    i8x4_dequant_bf16(w.x, sc, m128, lo.x, lo.y);
+    i8x4_dequant_bf16(w.y, sc, m128, lo.z, lo.w);
+    i8x4_dequant_bf16(w.z, sc, m128, hi.x, hi.y);
+    i8x4_dequant_bf16(w.w, sc, m128, hi.z, hi.w);
+  }
 }
 
 template <class C>
@@ -298,8 +313,8 @@ __device__ inline void store_i8_as(Stage<C>& sb, const Prefetch<C>& pf, float ks
     *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4 + 8) = hi;
   }
 }
-// Stages an INT8 tile: in fp16 (F16: K' = code x ks, V' = code x vs x
-// 2^-P_SHIFT; t.ok16 says whether every scale of the tile fits fp16's range,
+// Stages an INT8 tile: in fp16 (F16: K' = code x fp16(ks), V' = code x
+// fp16(vs x 2^-P_SHIFT), products rounded to fp16; t.ok16 says whether every scale of the tile fits fp16's range,
 // which every wave decides alike since each holds the scales of all the
 // tile's rows), or in bf16 (code x scale rounded to bf16).
 template <class C, bool F16>
