@@ -18,7 +18,10 @@
 // one contiguous 8 KB block).  A token-major cache, whose writes are as
 // contiguous as the reads, made this kernel 2-10% faster but the INT8
 // attention tiles (64 rows 2 KB apart) 5-7% slower on 1280x704 segments with
-// history, which costs far more.  (16-byte stores measured 9-13% faster than
+// history, which costs far more.  Gathering 128 rows (128 / H tokens x all
+// heads) per block in LDS and writing them head by head in runs of
+// contiguous bytes was slower still (3.55 against 4.73 TB/s at 337 MB).
+// (16-byte stores measured 9-13% faster than
 // 8-byte ones; non-temporal loads/stores, two rows per lane group, and blocks
 // of 32 consecutive tokens of one head, which write their codes and scales
 // contiguously but read rows 4 KB apart, were slower: the last by 10%; so was
