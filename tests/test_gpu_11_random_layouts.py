@@ -1,0 +1,80 @@
+"""GPU parity on 160 seeded random layouts.
+
+Each case draws a segment sequence (1-4 segments of 1-5 latent frames, 1-97
+tokens per frame, heads of 0-40 tokens, 0-3 action tails with random
+windows, some empty), a history window (or none), 1-4 attention heads,
+normal or heavy-tailed keys and values, sometimes a keep list, and the plan
+options (tile height, forced key splits for video and text tiles).  The
+cache is filled through hn_kv_quant_append and the query segment's video
+and text queries attend in one call; every row of both outputs and of the
+LSE is compared with the oracle at the bar.  The draws come from a fixed
+seed, so the cases are the same on every run; each prints its layout first.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import masked_attention_hn_amd as hn
+    import _gpu as G
+
+
+def _layout(seed):
+    rng = np.random.default_rng(1000 + seed)
+    n_seg = int(rng.integers(1, 5))
+    P = int(rng.choice([1, 7, 24, 50, 97]))
+    segs = []
+    for _ in range(n_seg):
+        F = int(rng.integers(1, 6))
+        head = int(rng.integers(0, 41))
+        m = int(rng.integers(0, 4))
+        tails = [int(rng.integers(0, 30)) for _ in range(m)]
+        wins = []
+        for _ in range(m):
+            a = int(rng.integers(0, F + 1))
+            b = int(rng.integers(a, F + 1))
+            wins.append((a, b))
+        segs.append(W._seg(F, P, head, tails, wins))
+    # mostly the last segment, so that most cases carry INT8 history
+    S = n_seg - 1 if rng.random() < 0.7 else int(rng.integers(0, n_seg))
+    hist = sum(s.frames for s in segs[:S])
+    window = None if rng.random() < 0.3 else int(rng.integers(1, max(2, hist + 2)))
+    heads = int(rng.integers(1, 5))
+    dist = "student_t4" if rng.random() < 0.4 else "normal"
+    keep = float(rng.choice([0.25, 0.5])) if rng.random() < 0.3 else None
+    w = W.Workload(f"rand{seed}", heads, segs, S, window, 500 + seed, kv_dist=dist, sparse_keep=keep,
+                   sparse_seed=(900 + seed) if keep else None)
+    # a keep list fixes 128-row query tiles
+    rows = int(rng.choice([0, 128] if keep else [0, 128, 256]))
+    opts = hn.PlanOpts(n_splits=int(rng.choice([0, 1, 2, 3])), n_splits_text=int(rng.choice([0, 1, 2])),
+                       tile_rows=rows)
+    return w, opts
+
+
+@pytest.mark.parametrize("seed", range(160))
+def test_random_layout(seed):
+    w, opts = _layout(seed)
+    cur = w.current
+    print(f"[random] seed {seed}: H={w.heads} S={w.query_segment} W={w.window} "
+          f"segments={[(s.frames, s.tokens_per_frame, s.head_len, s.action_len, s.action_f0, s.action_f1) for s in w.segments]} "
+          f"{w.kv_dist} keep={w.sparse_keep} opts=({opts.n_splits},{opts.n_splits_text},{opts.tile_rows})",
+          flush=True)
+    d = W.generate(w)
+    run = G.Run(w, d, opts=opts)
+    if cur.text_len > 0:
+        o, o_t, lse, lse_t = run.attn_joint()
+    else:
+        o, lse = run.attn()
+    if cur.video_len > 0:
+        ref, ref_lse, _ = oracle.attention(w, d)
+        G.check_bar(o.float().cpu().numpy(), ref, f"seed {seed} video")
+        assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-2
+    if cur.text_len > 0:
+        ref_t, ref_lse_t, _ = oracle.attention(w, d, queries="text")
+        G.check_bar(o_t.float().cpu().numpy(), ref_t, f"seed {seed} text")
+        assert np.abs(lse_t.cpu().numpy() - ref_lse_t).max() <= 1e-2
