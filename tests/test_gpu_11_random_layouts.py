@@ -7,7 +7,8 @@ normal or heavy-tailed keys and values, sometimes a keep list, and the plan
 options (tile height, forced key splits for video and text tiles).  The
 cache is filled through hn_kv_quant_append and the query segment's video
 and text queries attend in one call; every row of both outputs and of the
-LSE is compared with the oracle at the bar.  The draws come from a fixed
+LSE is compared with the oracle at the bar; the DENSE expansion of the plan
+and the cache's INT8 codes and scales bit for bit.  The draws come from a fixed
 seed, so the cases are the same on every run; each prints its layout first.
 """
 import numpy as np
@@ -78,3 +79,54 @@ def test_random_layout(seed):
         ref_t, ref_lse_t, _ = oracle.attention(w, d, queries="text")
         G.check_bar(o_t.float().cpu().numpy(), ref_t, f"seed {seed} text")
         assert np.abs(lse_t.cpu().numpy() - ref_lse_t).max() <= 1e-2
+    _check_mask(w, d, run)
+    _check_cache(w, d, run.cache)
+
+
+def _check_mask(w, d, run):
+    """DENSE expansion of the plan (video rows, then text rows) bit for bit
+    against the oracle's explicit masks in the canonical key order, and the
+    plan's pair count against the oracle's."""
+    cur = w.current
+    csr = d.get("csr") if w.sparse_keep is not None else None
+    cols = G.canonical_columns(w)
+    ref = oracle.mask(w, None, csr)
+    if cur.text_len > 0:
+        ref = np.concatenate([ref, oracle.mask_text(w)])
+    absent = np.ones(ref.shape[1], bool)
+    absent[cols] = False
+    assert not ref[:, absent].any()
+    got = run.dense(0, cur.video_len + cur.text_len)
+    assert np.array_equal(got, ref[:, cols])
+    if csr is None:  # a keep-list plan reports -1 (its count depends on the list)
+        assert run.plan.visible_pairs * 4 * 128 * w.heads == oracle.effective_flops(w)
+    else:
+        assert run.plan.visible_pairs == -1
+    if cur.text_len > 0:
+        assert run.plan.visible_pairs_text * 4 * 128 * w.heads == oracle.effective_flops_text(w)
+
+
+def _check_cache(w, d, cache):
+    """Ring frames in the window and the whole head store, codes and scales,
+    bit for bit against the oracle quantizer."""
+    S, P, Wf = w.query_segment, w.current.tokens_per_frame, w.ring_frames
+    src = [(s, f) for s in range(S) for f in range(w.segments[s].frames)]
+    fs = len(src)
+    H = w.heads
+    for g in range(fs - min(fs, Wf), fs):
+        s, f = src[g]
+        slot = g % Wf
+        for nm, codes, scales in (("k_vid", cache.ring_k, cache.ring_ks), ("v_vid", cache.ring_v, cache.ring_vs)):
+            q, sc = oracle.quantize(d["segments"][s][nm][f * P:(f + 1) * P])
+            got_q = codes[:, slot * P:(slot + 1) * P].cpu().numpy().transpose(1, 0, 2)
+            got_s = scales[:, slot * P:(slot + 1) * P].cpu().numpy().T
+            assert np.array_equal(got_q, q) and np.array_equal(got_s.view(np.uint32), sc.view(np.uint32))
+    off = 0
+    for s in range(S):
+        hl = w.segments[s].head_len
+        for nm, codes, scales in (("k_txt", cache.heads_k, cache.heads_ks), ("v_txt", cache.heads_v, cache.heads_vs)):
+            q, sc = oracle.quantize(d["segments"][s][nm][:hl])
+            got_q = codes[:, off:off + hl].cpu().numpy().transpose(1, 0, 2).reshape(hl, H, 128)
+            got_s = scales[:, off:off + hl].cpu().numpy().T.reshape(hl, H)
+            assert np.array_equal(got_q, q) and np.array_equal(got_s.view(np.uint32), sc.view(np.uint32))
+        off += hl
