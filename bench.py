@@ -44,6 +44,10 @@ def parse():
                     help="query rows the oracle computes (default: about 10-30 s of CPU work)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the joint, camera and archive measurements (counter runs)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="key splits per video query tile (0 = the library's automatic choice)")
+    ap.add_argument("--text-splits", type=int, default=0,
+                    help="key splits per text query tile (0 = automatic)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -191,7 +195,8 @@ def main():
         csr = data["csr"]
         sparse = hn.BlockSparse(torch.from_numpy(csr["row_ptr"]), torch.from_numpy(csr["col"]),
                                 csr["n_qtiles"])
-    ws = torch.empty(hn.hn_attn_workspace_size(cache, seg, sparse), dtype=torch.uint8, device=dev)
+    opts = hn.PlanOpts(n_splits=args.splits, n_splits_text=args.text_splits)
+    ws = torch.empty(hn.hn_attn_workspace_size(cache, seg, sparse, opts), dtype=torch.uint8, device=dev)
     plan_c = hn.hn_tile_plan()
     plan = hn.Plan(ws, plan_c)
     saved = (cache.c.frames_seen, cache.c.head_tokens, cache.c.segments)
@@ -203,7 +208,7 @@ def main():
 
     def step(i=None, timed=False):
         cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
-        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c)
+        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c, opts=opts)
         if timed:
             ev_a0[i].record(stream)
         hn.hn_seg_attn_fwd(cache, seg, plan, q, k_txt, v_txt, k_vid, v_vid, o)
@@ -379,7 +384,7 @@ def main():
     joint = None
     if w.current.text_len > 0 and not args.no_extras:
         cache.c.frames_seen, cache.c.head_tokens, cache.c.segments = saved
-        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c)
+        hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c, opts=opts)
         q_txt = to_dev(data["q_txt"])
         o_txt = torch.empty_like(q_txt)
         pairs_t = visible_pairs_text(w)
@@ -431,6 +436,8 @@ def main():
             }.get(args.workload, args.workload),
             "name": args.workload,
             "step": "tile plan + attention + INT8 quantize/append",
+            "key_splits": args.splits or "automatic",
+            "key_splits_text": args.text_splits or "automatic",
             "effective_flop_per_step": flops,
             "visible_pairs_per_head": pairs,
         },
