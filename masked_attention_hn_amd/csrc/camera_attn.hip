@@ -47,11 +47,14 @@ __device__ inline float sum_lanes(float x) {
 
 __global__ __launch_bounds__(256) void camera_attn_kernel(CameraParams p) {
   const int lane = threadIdx.x & (LANES - 1);
-  const int64_t unit = (int64_t)blockIdx.x * ROWS + (threadIdx.x / LANES);
+  // a block takes ROWS consecutive tokens of one head, so that its lane
+  // groups read the same camera rows (one fetch from L2, the rest from the
+  // CU's cache); consecutive blocks take the heads of the same tokens
+  const int64_t tb = blockIdx.x / p.H;
+  const int h = (int)(blockIdx.x - tb * p.H);
+  const int64_t t = tb * ROWS + (threadIdx.x / LANES);
   // whole lane groups leave together, so the butterflies stay inside active lanes
-  if (unit >= p.rows * p.H) return;
-  const int64_t t = unit / p.H;
-  const int h = (int)(unit - t * p.H);
+  if (t >= p.rows) return;
   const int f = (int)(t / p.P);
   const int lo = max(0, f - p.radius);
   const int hi = min(p.F, f + p.radius + 1);
@@ -98,9 +101,8 @@ __global__ __launch_bounds__(256) void camera_attn_kernel(CameraParams p) {
 }  // namespace
 
 hipError_t launch_camera_attn(const CameraParams& p, hipStream_t s) {
-  const int64_t units = p.rows * p.H;
-  if (units == 0) return hipSuccess;
-  const int64_t blocks = (units + ROWS - 1) / ROWS;
+  if (p.rows == 0 || p.H == 0) return hipSuccess;
+  const int64_t blocks = (p.rows + ROWS - 1) / ROWS * p.H;
   hipLaunchKernelGGL(camera_attn_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
