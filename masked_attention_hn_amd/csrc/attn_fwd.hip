@@ -35,13 +35,14 @@
 //            MFMA rate; the power-of-two shifts keep K', V' and P inside
 //            fp16's range.  A tile whose scales would leave that range (|K|
 //            above 65,024 or |V| above 8.3e6) falls back to bf16 K and V.
-//   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (each lane then holds
-//            the tile's keys for one query, so the row max/sum are in-lane plus
-//            one v_permlane32_swap with lane^32); online softmax in the log2
-//            domain with the score scale folded into the exp2 argument; the
-//            probabilities are packed to bf16 in registers and used directly
-//            as the B operand of O^T = V^T P^T, whose accumulator keeps each
-//            query's 128 outputs in its own lane pair.
+//   math   = S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (_f16 on the INT8
+//            tiles; each lane then holds the tile's keys for one query, so the
+//            row max/sum are in-lane plus one v_permlane32_swap with lane^32);
+//            online softmax in the log2 domain with the score scale folded into
+//            the exp2 argument; the probabilities are packed to bf16 (fp16 on
+//            INT8 tiles) in registers and used directly as the B operand of
+//            O^T = V^T P^T, whose accumulator keeps each query's 128 outputs
+//            in its own lane pair.
 //   rescale= lazy: the running max only moves (and O, l are rescaled) when a
 //            row's tile max exceeds it by more than 8 in log2 units, so
 //            probabilities stay <= 2^8 and the rescale is rare after the
