@@ -347,9 +347,10 @@ hn_status hn_attn_mask_build(const hn_kv_cache* cache, const hn_seg_layout* seg,
  * [T] "单卡 4090 怎么做到的", first technique).  16-bit MFMA with fp32
  * accumulation and online softmax: the segment's own tiles in BF16 (its
  * inputs' type); the history tiles in FP16 (q times the scale rounded to
- * FP16, the product rounded to FP16: within 2^-10 of q*scale, against an
- * FP16 copy of Q), which keeps the history nearly as close to q*scale as the
- * segment's own values are to their inputs.  The
+ * FP16, the product rounded to FP16: within 2^-10 of q*scale for rows whose
+ * largest |value| is at least 0.0078, within 4e-6 absolute below that,
+ * against an FP16 copy of Q), which keeps the history nearly as close to
+ * q*scale as the segment's own values are to their inputs.  The
  * FP16 path holds history values with |K| <= 65,024 and |V| <= 8.3e6; a tile
  * outside that range sends its query tile through BF16 for every key.
  *

@@ -27,7 +27,7 @@
 //            per-token fp32 scales and dequantized in registers on their way
 //            into LDS, so the math never sees a scale.  They are staged and
 //            multiplied in fp16, not bf16: K' = fp16(code x fp16(scale)) and
-//            V' = fp16(code x fp16(scale x 2^-7)), in packed fp16 arithmetic,
+//            V' = fp16(code x 2^-7 x fp16(scale)), in packed fp16 arithmetic,
 //            against an fp16 copy of Q and fp16 probabilities that carry the
 //            2^7 back.  fp16 keeps 11 significant bits where bf16 keeps 8,
 //            which bounds the error of the dequantized history 4x tighter (two
@@ -73,11 +73,11 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag
 // fp16 staging of INT8 tiles.  Probabilities are <= 2^RESCALE_SLACK, so with
 // the 2^7 shift they stay <= 2^15; codes are <= 127 in magnitude, so
-// K' = code x ks fits fp16 (max 65504) for ks <= 512 and V' = code x vs x 2^-7
-// for vs <= 65536.
+// K' = code x ks fits fp16 (max 65504) for ks <= 512, and V' = code x 2^-7 x
+// vs for any scale fp16 holds (vs <= 65504).
 constexpr float P_SHIFT = 7.0f;
 constexpr float KS_MAX_F16 = 512.0f;
-constexpr float VS_MAX_F16 = 65536.0f;
+constexpr float VS_MAX_F16 = 65504.0f;
 template <int NW_, int QB_, int KT_>
 struct Cfg {
   static constexpr int NW = NW_, QB = QB_, KT = KT_;
@@ -163,31 +163,44 @@ __device__ inline void i8x4_dequant_bf16(uint32_t w, float sc, float m128, uint3
 // Four INT8 codes of w times the fp16 row scale s2 -> two packed fp16 pairs,
 // in packed fp16 arithmetic: the byte u = q + 128 placed under the fp16
 // exponent of 1024 is the fp16 value 1024 + u (ulp 1 there), so one byte
-// permute makes two of them, one packed subtraction of 1152 gives q exactly,
-// and one packed multiply gives fp16(q x s2), rounded once.  (7 VALU
-// operations per 4 codes against 11 for the fp32 product and conversion.)
+// permute makes two of them, one packed subtraction of 1152 gives q exactly
+// (SHIFT: one packed fma x 2^-7 - 9 gives q x 2^-7 exactly), and one packed
+// multiply gives fp16(q x s2) (x 2^-7), rounded once.  (7 VALU operations
+// per 4 codes against 11 for the fp32 product and conversion.)  The shift
+// goes on the exact code, not on the scale, so that scales of rows with
+// |V| >= 0.0078 stay in fp16's normal range.
+template <bool SHIFT>
 __device__ inline void i8x4_dequant_f16(uint32_t w, f16x2 s2, uint32_t& p0, uint32_t& p1) {
   const uint32_t u = w ^ 0x80808080u;
   // bytes 4-7 of the permute's source are 0x64: codes 0, 1 -> halves of p0
-  const uint32_t e0 = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
-  const uint32_t e1 = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
-  const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
-  const f16x2 q0 = __builtin_bit_cast(f16x2, e0) - bias;
-  const f16x2 q1 = __builtin_bit_cast(f16x2, e1) - bias;
+  const f16x2 e0 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u));
+  const f16x2 e1 = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u));
+  f16x2 q0, q1;
+  if constexpr (SHIFT) {
+    const f16x2 sh = {(_Float16)0x1p-7f, (_Float16)0x1p-7f};
+    const f16x2 nine = {(_Float16)-9.0f, (_Float16)-9.0f};
+    q0 = __builtin_elementwise_fma(e0, sh, nine);  // (1024 + u) / 128 - 9 = q / 128
+    q1 = __builtin_elementwise_fma(e1, sh, nine);
+  } else {
+    const f16x2 bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+    q0 = e0 - bias;
+    q1 = e1 - bias;
+  }
   p0 = __builtin_bit_cast(uint32_t, q0 * s2);
   p1 = __builtin_bit_cast(uint32_t, q1 * s2);
 }
 // 16 INT8 codes of one row -> 16 dequantized 16-bit values (two 16-byte
-// words): fp16 (F16, scale rounded to fp16 first) or bf16.
-template <bool F16>
+// words): fp16 (F16, scale rounded to fp16 first; SHIFT: times 2^-7) or
+// bf16.
+template <bool F16, bool SHIFT = false>
 __device__ inline void i8x16_dequant(uint4 w, float sc, uint4& lo, uint4& hi) {
   if constexpr (F16) {
     const _Float16 h = (_Float16)sc;
     const f16x2 s2 = {h, h};
-    i8x4_dequant_f16(w.x, s2, lo.x, lo.y);
-    i8x4_dequant_f16(w.y, s2, lo.z, lo.w);
-    i8x4_dequant_f16(w.z, s2, hi.x, hi.y);
-    i8x4_dequant_f16(w.w, s2, hi.z, hi.w);
+    i8x4_dequant_f16<SHIFT>(w.x, s2, lo.x, lo.y);
+    i8x4_dequant_f16<SHIFT>(w.y, s2, lo.z, lo.w);
+    i8x4_dequant_f16<SHIFT>(w.z, s2, hi.x, hi.y);
+    i8x4_dequant_f16<SHIFT>(w.w, s2, hi.z, hi.w);
   } else {
     const float m128 = -128.0f * sc;
     i8x4_dequant_bf16(w.x, sc, m128, lo.x, lo.y);
@@ -306,7 +319,7 @@ __device__ inline void store_i8_as(Stage<C>& sb, const Prefetch<C>& pf, float ks
     __bf16* kblk = &sb.k[(kb32 * 8 + dch) * 512];
     *reinterpret_cast<uint4*>(kblk + q32 * 8) = lo;
     *reinterpret_cast<uint4*>(kblk + (32 + q32) * 8) = hi;
-    i8x16_dequant<F16>(pf.v[c8], vs, lo, hi);
+    i8x16_dequant<F16, F16>(pf.v[c8], vs, lo, hi);  // fp16 V carries 2^-P_SHIFT
     // columns 16 dch .. +16 -> c = dch / 2, G&1 = dch % 2, slots 16G + 4qq + {0..3}
     const int c = dch >> 1, G = 2 * g + (dch & 1);
     __bf16* vblk = &sb.v[(((c * C::KB + kb32) * 2 + h) * 2 + half) * 256];
@@ -314,10 +327,11 @@ __device__ inline void store_i8_as(Stage<C>& sb, const Prefetch<C>& pf, float ks
     *reinterpret_cast<uint4*>(vblk + (16 * G + 4 * qq) * 4 + 8) = hi;
   }
 }
-// Stages an INT8 tile: in fp16 (F16: K' = code x fp16(ks), V' = code x
-// fp16(vs x 2^-P_SHIFT), products rounded to fp16; t.ok16 says whether every scale of the tile fits fp16's range,
-// which every wave decides alike since each holds the scales of all the
-// tile's rows), or in bf16 (code x scale rounded to bf16).
+// Stages an INT8 tile: in fp16 (F16: K' = code x fp16(ks), V' = code x 2^-
+// P_SHIFT x fp16(vs), products rounded to fp16; t.ok16 says whether every
+// scale of the tile fits fp16's range, which every wave decides alike since
+// each holds the scales of all the tile's rows), or in bf16 (code x scale
+// rounded to bf16).
 template <class C, bool F16>
 __device__ inline void store_i8(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf) {
   static_assert(C::RG == 1, "the staging decision needs every row's scale in every wave");
@@ -325,7 +339,7 @@ __device__ inline void store_i8(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf
   const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
   if constexpr (F16) {
     t.ok16 = !__any(!(ks <= KS_MAX_F16 && vs <= VS_MAX_F16));
-    store_i8_as<C, true>(sb, pf, ks, vs * 0x1p-7f);
+    store_i8_as<C, true>(sb, pf, ks, vs);
   } else {
     store_i8_as<C, false>(sb, pf, ks, vs);
   }

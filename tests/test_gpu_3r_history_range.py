@@ -21,6 +21,12 @@ new), so that the restart happens before any step, after an odd and after an
 even number of fp16 steps.  The oracle computes the same modified inputs.
 Staged in fp16 the planted key would overflow (127 x 1032 > 65,504), so the
 outputs meet the bar only if the block restarted in bf16.
+
+Small values: every value (history and current) scaled by 2^-9 scales O by
+2^-9 in exact arithmetic and leaves the scores alone, so 2^9 x O must meet
+the bar of the oracle on the unscaled inputs.  This holds only if the fp16
+staging keeps small scales in fp16's normal range (a value scale of 3e-4 x
+2^-7 would be subnormal and lose up to 8% of its bits).
 """
 import math
 
@@ -111,3 +117,23 @@ def test_huge_history_key_restarts_in_bf16(name, place, rows):
     opts = None if rows == "auto" else hn.PlanOpts(tile_rows=int(rows))
     run = G.Run(w, d, opts=opts)
     _check(w, d, *_joint(run, 0), f"{name} {place}")
+
+
+@pytest.mark.parametrize("name", ["m1", "m2", "c3_h2"])
+def test_small_values_keep_precision(name):
+    print(f"[range] small values {name}", flush=True)
+    w = W.config(name)
+    d = W.generate(w)
+    ref_o, ref_lse, _ = oracle.attention(w, d, G.sample_rows(w.current.video_len)
+                                         if w.current.video_len > 4096 else None)
+    for seg in d["segments"]:
+        for nm in ("v_txt", "v_vid"):
+            x = W.bf16_bits_to_f32(seg[nm]) * np.float32(2.0 ** -9)
+            seg[nm] = W.f32_to_bf16_bits(x)       # exact: a power of two
+    run = G.Run(w, d)
+    o, lse = run.attn()
+    rows = G.sample_rows(w.current.video_len) if w.current.video_len > 4096 else np.arange(w.current.video_len)
+    got = o.float().cpu().numpy()[rows] * 2.0 ** 9
+    err = G.check_bar(got, ref_o, f"{name} V x 2^-9")
+    assert np.abs(lse.cpu().numpy()[:, rows] - ref_lse).max() <= 1e-2
+    print(f"  {name}: max-abs of 2^9 O {err.max():.3e}", flush=True)
