@@ -137,3 +137,45 @@ def test_small_values_keep_precision(name):
     err = G.check_bar(got, ref_o, f"{name} V x 2^-9")
     assert np.abs(lse.cpu().numpy()[:, rows] - ref_lse).max() <= 1e-2
     print(f"  {name}: max-abs of 2^9 O {err.max():.3e}", flush=True)
+
+
+@pytest.mark.parametrize("name", ["m1", "m2"])
+def test_key_scale_invariance_bitwise(name):
+    """Keys scaled by 2^-4 with sm_scale scaled by 2^4 leave every score
+    unchanged: the INT8 codes are the same, the scales exactly 2^-4 times
+    theirs, fp16(code x fp16(scale)) and the bf16 keys exactly 2^-4 times
+    theirs (all in fp16's normal range for unit-variance rows), and the
+    products and sums scale exactly.  So the outputs must equal those of the
+    unscaled inputs bit for bit."""
+    print(f"[range] key scale {name}", flush=True)
+    w = W.config(name)
+    d = W.generate(w)
+    run = G.Run(w, d)
+    ref = run.attn_joint()
+    for seg in d["segments"]:
+        for nm in ("k_txt", "k_vid"):
+            seg[nm] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(seg[nm]) * np.float32(2.0 ** -4))
+    run2 = G.Run(w, d)
+    got = hn.seg_attn_joint(run2.cache, run2.seg, run2.plan, run2.q, run2.q_txt, run2.k_txt, run2.v_txt,
+                            run2.k_vid, run2.v_vid, sm_scale=SM * 2.0 ** 4)
+    torch.cuda.synchronize()
+    for x, y in zip(got, ref):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("name", ["m1", "m2"])
+def test_large_values_keep_precision(name):
+    """Every value scaled by 2^12 (up to |V| ~ 10^5 on heavy tails, inside the
+    fp16 staging's range): 2^-12 O must meet the bar of the oracle on the
+    unscaled inputs."""
+    print(f"[range] large values {name}", flush=True)
+    w = W.config(name)
+    d = W.generate(w)
+    ref_o, ref_lse, _ = oracle.attention(w, d)
+    for seg in d["segments"]:
+        for nm in ("v_txt", "v_vid"):
+            seg[nm] = W.f32_to_bf16_bits(W.bf16_bits_to_f32(seg[nm]) * np.float32(2.0 ** 12))
+    run = G.Run(w, d)
+    o, lse = run.attn()
+    G.check_bar(o.float().cpu().numpy() * 2.0 ** -12, ref_o, f"{name} V x 2^12")
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-2
