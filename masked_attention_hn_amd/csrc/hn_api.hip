@@ -106,10 +106,13 @@ int device_cus() {
 // about a quarter of an unsplit task's time.  It pays where the grid leaves
 // the last round of blocks partly empty and half-length tasks fill it:
 //   1280x704 steady state, 16 heads: 1,664 blocks of 256 rows = 6.5 rounds on
-//     256 CUs; 1 / 2 / 3 splits 10.09 / 9.77 / 10.73 ms per launch, and the
-//     7th segment (158k INT8 history keys) 44.86 / 43.16 ms at 1 / 2;
-//   its 2-head share: 208 blocks, one round; 1 / 5 / 6 / 7 splits
-//     1.238 / 1.398 / 1.363 / 1.386 ms.
+//     256 CUs; 1 / 2 / 3 / 4 splits 10.22 / 9.60 / 10.48 / 9.95 ms per
+//     launch, and the 7th segment (158k INT8 history keys) 44.77 / 42.13 /
+//     44.28 / 42.80 ms;
+//   its 2-head share: 208 blocks, one round; 1 / 2 / 3 / 4 splits
+//     1.270 / 1.380 / 1.384 / 1.466 ms;
+//   the 480x832 segment: 736 blocks, 2.9 rounds; 1 / 2 splits 1.059 /
+//     1.129 ms.
 // With r_s = rounds of the s-split grid, two splits are taken when
 // r_2 / 2 + 1/4 < r_1 and each half keeps at least 8192 keys.  A grid of at
 // most one block per two CUs is split to about one block per CU, with no
