@@ -203,6 +203,14 @@ def main():
     pairs = visible_pairs(w, csr)
     flops = 4.0 * 128 * pairs * w.heads
 
+    # one call on the cache as the history left it, before any step appends
+    # (each step re-appends this segment, which in a full window overwrites
+    # the oldest history frames: same work, other data), kept for the CPU
+    # leg's parity check
+    o_check = torch.empty_like(q)
+    hn.hn_attn_mask_build(cache, seg, sparse, hn.HN_MASK_TILE_PLAN, 0, 0, ws, plan_c, opts=opts)
+    hn.hn_seg_attn_fwd(cache, seg, plan, q, k_txt, v_txt, k_vid, v_vid, o_check)
+
     ev_a0 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ev_a1 = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
 
@@ -473,8 +481,20 @@ def main():
         rows = np.linspace(0, w.current.video_len - 1, min(n_rows, w.current.video_len)).astype(int)
         rows = np.unique(rows)
         tc0 = time.perf_counter()
-        oracle.attention(w, data, rows)
+        ref, _, _ = oracle.attention(w, data, rows)
         tc = time.perf_counter() - tc0
+        # the same rows of the GPU output against it (max-abs 2e-2, plus half a
+        # bf16 ulp where |O_ref| >= 8; mean-abs 2e-3)
+        got = o_check.float().cpu().numpy()[rows]
+        err = np.abs(got - ref)
+        half_ulp = np.where(np.abs(ref) >= 8.0,
+                            2.0 ** (np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 8), 0.0)
+        parity = {
+            "rows": int(len(rows)),
+            "max_abs": float(f"{err.max():.4e}"),
+            "mean_abs": float(f"{err.mean():.4e}"),
+            "within_bar": bool((err <= 2e-2 + half_ulp).all() and err.mean() <= 2e-3),
+        }
         if csr is None:
             per_row = pairs / w.current.video_len
             sample_pairs = per_row * len(rows)
@@ -506,6 +526,7 @@ def main():
             "kind": "oracle",
             "cpu": cpu_model,
             "cores_available": avail,
+            "gpu_parity": parity,
             "sample": f"{len(rows)} of {w.current.video_len} query rows (evenly spaced), all "
                       f"{w.heads} heads, fp64 numpy oracle incl. key preparation; {tc:.1f} s; "
                       "its products run on the BLAS threads, the rest on one thread",
