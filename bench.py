@@ -48,6 +48,8 @@ def parse():
                     help="key splits per video query tile (0 = the library's automatic choice)")
     ap.add_argument("--text-splits", type=int, default=0,
                     help="key splits per text query tile (0 = automatic)")
+    ap.add_argument("--tile-rows", type=int, default=0,
+                    help="query rows per tile of a plan without keep list: 128, 256 or 384 (0 = automatic)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -195,7 +197,7 @@ def main():
         csr = data["csr"]
         sparse = hn.BlockSparse(torch.from_numpy(csr["row_ptr"]), torch.from_numpy(csr["col"]),
                                 csr["n_qtiles"])
-    opts = hn.PlanOpts(n_splits=args.splits, n_splits_text=args.text_splits)
+    opts = hn.PlanOpts(n_splits=args.splits, n_splits_text=args.text_splits, tile_rows=args.tile_rows)
     ws = torch.empty(hn.hn_attn_workspace_size(cache, seg, sparse, opts), dtype=torch.uint8, device=dev)
     plan_c = hn.hn_tile_plan()
     plan = hn.Plan(ws, plan_c)
@@ -446,6 +448,7 @@ def main():
             "step": "tile plan + attention + INT8 quantize/append",
             "key_splits": args.splits or "automatic",
             "key_splits_text": args.text_splits or "automatic",
+            "tile_rows": args.tile_rows or "automatic",
             "effective_flop_per_step": flops,
             "visible_pairs_per_head": pairs,
         },

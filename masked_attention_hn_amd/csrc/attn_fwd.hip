@@ -70,6 +70,15 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+#ifndef HN_QLI_KLOOK
+#define HN_QLI_KLOOK 3
+#endif
+#ifndef HN_QLI_VLOOK
+#define HN_QLI_VLOOK 4
+#endif
+#ifndef HN_QLI_QLOOK
+#define HN_QLI_QLOOK 2
+#endif
 constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag
 // fp16 staging of INT8 tiles.  Probabilities are <= 2^RESCALE_SLACK, so with
 // the 2^7 shift they stay <= 2^15; codes are <= 127 in magnitude, so
@@ -78,20 +87,25 @@ constexpr float RESCALE_SLACK = 8.0f;  // log2 units the running max may lag
 constexpr float P_SHIFT = 7.0f;
 constexpr float KS_MAX_F16 = 512.0f;
 constexpr float VS_MAX_F16 = 65504.0f;
-template <int NW_, int QB_, int KT_>
+// QL: Q lives in LDS (each wave's rows in a region of its own, operand-major)
+// instead of registers; the first SW waves stage the tiles.
+template <int NW_, int QB_, int KT_, bool QL_ = false, int SW_ = NW_>
 struct Cfg {
-  static constexpr int NW = NW_, QB = QB_, KT = KT_;
+  static constexpr int NW = NW_, QB = QB_, KT = KT_, SW = SW_;
+  static constexpr bool QL = QL_;
   static constexpr int T = 64 * NW;            // threads per block
   static constexpr int ROWS = 32 * QB * NW;    // query rows per block
   static constexpr int KB = KT / 32;           // 32-key blocks per tile
   static constexpr int KBLK = KB * 8;          // 1 KB K-operand blocks per tile
   static constexpr int VBLK = 4 * KB * 2;      // 1 KB V-operand block pairs per tile
-  static constexpr int CH8 = 8 * KT / T;       // INT8 16-byte chunks per thread (K and V each)
+  static constexpr int CH8 = 8 * KT / (64 * SW);  // INT8 16-byte chunks per staging thread (K and V each)
   static constexpr int RG = KT / 64;           // INT8 staging: 64-row groups; wave w takes rows
-                                               // 64 (w % RG) + lane, chunks of 16 codes w / RG + c NW/RG
+                                               // 64 (w % RG) + lane, chunks of 16 codes w / RG + c SW/RG
   static_assert(KT == 64 || KT == 128, "tile shape");
-  static_assert(KBLK % NW == 0 && VBLK % NW == 0 && CH8 >= 1 && NW % RG == 0, "load split");
+  static_assert(SW <= NW && SW % 4 == 0, "staging waves: whole SIMD rounds");
+  static_assert(KBLK % SW == 0 && VBLK % SW == 0 && CH8 >= 1 && SW % RG == 0, "load split");
   static_assert(2 * KT <= T, "one scale per thread");
+  static_assert(!QL || QB == 1, "Q in LDS: one 32-row block per wave");
 };
 
 // LDS tiles are stored operand-major, so that every operand read of a wave is
@@ -111,6 +125,13 @@ template <class C>
 struct Stage {
   __bf16 k[C::KT * D];
   __bf16 v[C::KT * D];
+};
+// Q of the block in LDS (QL): wave w's 32 rows at [w * 32 * D, ...), 16-d
+// chunk t as the 1 KB B operand of the QK MFMA (slot lane = 32g + q holds
+// Q[q][16t + 8g .. +8]).
+template <class C>
+struct QStore {
+  __bf16 q[C::QL ? C::ROWS * D : 8];
 };
 
 struct TileDesc {
@@ -265,13 +286,13 @@ __device__ inline void load_bf16(const Sources& S, rsrc_t rk, rsrc_t rv, int kb,
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar offsets
   const uint32_t base = (uint32_t)kb * S.tok_bytes;
 #pragma unroll
-  for (int j = 0; j < C::KBLK / C::NW; ++j) {
-    const int blk = wave * (C::KBLK / C::NW) + j;          // (kb32, t) = (blk / 8, blk % 8)
+  for (int j = 0; j < C::KBLK / C::SW; ++j) {
+    const int blk = wave * (C::KBLK / C::SW) + j;          // (kb32, t) = (blk / 8, blk % 8)
     ld_lds16(rk, &sb.k[blk * 512], S.vo_k, base + (blk >> 3) * 32 * S.tok_bytes + (blk & 7) * 32);
   }
 #pragma unroll
-  for (int j = 0; j < C::VBLK / C::NW; ++j) {
-    const int pr = wave * (C::VBLK / C::NW) + j;           // ((c*KB + kb32)*2 + h)
+  for (int j = 0; j < C::VBLK / C::SW; ++j) {
+    const int pr = wave * (C::VBLK / C::SW) + j;           // ((c*KB + kb32)*2 + h)
     const int c = pr / (2 * C::KB), kb32 = (pr / 2) % C::KB, h = pr & 1;
     ld_lds16(rv, &sb.v[pr * 512], S.vo_v, base + (kb32 * 32 + 16 * h) * S.tok_bytes + 64 * c);
   }
@@ -284,11 +305,13 @@ __device__ inline void load_i8(const Sources& S, rsrc_t rk, rsrc_t rv, rsrc_t rk
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = wave % C::RG;                         // row group of this wave
   const uint32_t base = (uint32_t)(kb + 64 * rg) * D;
+  if (C::SW == C::NW || wave < C::SW) {
 #pragma unroll
-  for (int c = 0; c < C::CH8; ++c) {
-    const uint32_t dch = c * (C::NW / C::RG) + wave / C::RG;  // 16-code chunk of row 64 rg + lane
-    pf.k[c] = ld_b128(rk, S.vo_i, base + dch * 16);
-    pf.v[c] = ld_b128(rv, S.vo_i, base + dch * 16);
+    for (int c = 0; c < C::CH8; ++c) {
+      const uint32_t dch = c * (C::SW / C::RG) + wave / C::RG;  // 16-code chunk of row 64 rg + lane
+      pf.k[c] = ld_b128(rk, S.vo_i, base + dch * 16);
+      pf.v[c] = ld_b128(rv, S.vo_i, base + dch * 16);
+    }
   }
   // every thread dequantizes its row, so every thread needs its scales
   // (vo_sc = (tid % KT) * 4 addresses row 64 rg + lane)
@@ -312,7 +335,7 @@ __device__ inline void store_i8_as(Stage<C>& sb, const Prefetch<C>& pf, float ks
   const int h = (r >> 4) & 1, half = (r >> 3) & 1, g = (r >> 2) & 1, qq = r & 3;
 #pragma unroll
   for (int c8 = 0; c8 < C::CH8; ++c8) {
-    const int dch = c8 * (C::NW / C::RG) + wave / C::RG;
+    const int dch = c8 * (C::SW / C::RG) + wave / C::RG;
     uint4 lo, hi;
     i8x16_dequant<F16>(pf.k[c8], ks, lo, hi);
     // d chunks 2dch (g=0) and 2dch+1 (g=1) of K block (kb32, t = dch)
@@ -337,11 +360,12 @@ __device__ inline void store_i8(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf
   static_assert(C::RG == 1, "the staging decision needs every row's scale in every wave");
   // rows past the tile's valid keys become zeros
   const float ks = pf.ok ? pf.ks : 0.0f, vs = pf.ok ? pf.vs : 0.0f;
+  const bool stager = C::SW == C::NW || __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) < C::SW;
   if constexpr (F16) {
     t.ok16 = !__any(!(ks <= KS_MAX_F16 && vs <= VS_MAX_F16));
-    store_i8_as<C, true>(sb, pf, ks, vs);
+    if (stager) store_i8_as<C, true>(sb, pf, ks, vs);
   } else {
-    store_i8_as<C, false>(sb, pf, ks, vs);
+    if (stager) store_i8_as<C, false>(sb, pf, ks, vs);
   }
 }
 
@@ -351,6 +375,7 @@ __device__ inline void store_i8(TileDesc& t, Stage<C>& sb, const Prefetch<C>& pf
 template <class C, int I8>
 __device__ inline void start_tile(const Sources& S, const TileDesc& t, Stage<C>& sb, Prefetch<C>& pf) {
   if (t.src >= SRC_TXT) {
+    if (C::SW < C::NW && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >= C::SW) return;
     if (t.src == SRC_VID) load_bf16<C>(S, S.k_vid, S.v_vid, t.kb, sb);
     else load_bf16<C>(S, S.k_txt, S.v_txt, t.kb, sb);
   } else if constexpr (I8 != 0) {
@@ -412,8 +437,12 @@ struct RowState {
 // and PV MFMAs of the blocks form one straight-line region.  The row sum adds
 // the 16-bit probabilities the PV MFMA consumes, so their rounding cancels in
 // O = acc / l.  scale[q] is the score scale (log2 units) of query block q.
-template <class C, bool MASK, bool QK16, bool PV16>
-__device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8],
+// With Q in LDS (QL) the QK loop reads the wave's Q chunks from qw (the
+// lane's slot of chunk 0), QLOOK chunks ahead, instead of qreg.  TIGHT: the
+// kernel also carries INT8 staging registers, and the operand lookaheads are
+// shortened to fit its 168 VGPRs without spilling.
+template <class C, bool MASK, bool QK16, bool PV16, bool TIGHT = false>
+__device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8], const __bf16* qw,
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
                                           const float (&scale)[C::QB], int nk, const bool (&row_ok)[C::QB]) {
   constexpr int QB = C::QB, KB = C::KB;
@@ -433,8 +462,13 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   // to itself the compiler reads one or two ahead and waits on LDS): +2% on
   // the 480x832 segment and on the 1280x704 steady state.
   {
-    constexpr int NK = 8 * KB, KLOOK = 5;
+    constexpr int NK = 8 * KB, KLOOK = TIGHT ? HN_QLI_KLOOK : 5, QLOOK = TIGHT ? HN_QLI_QLOOK : 2;
     bf16x8 kk[NK];
+    bf16x8 qq[8];
+    if constexpr (C::QL) {
+#pragma unroll
+      for (int t = 0; t < QLOOK; ++t) qq[t] = ld8(qw + t * 512);
+    }
 #pragma unroll
     for (int i = 0; i < KLOOK; ++i) kk[i] = ld8(kl + ((i % KB) * 8 + i / KB) * 512);
 #pragma unroll
@@ -442,13 +476,17 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
       const int t = i / KB, kb = i % KB;
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
+        const bf16x8 qop = C::QL ? qq[t] : qreg[q][t];
         if constexpr (QK16)
           s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kk[i]),
-                                                            __builtin_bit_cast(f16x8, qreg[q][t]), s[q][kb], 0, 0, 0);
+                                                            __builtin_bit_cast(f16x8, qop), s[q][kb], 0, 0, 0);
         else
-          s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[i], qreg[q][t], s[q][kb], 0, 0, 0);
+          s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kk[i], qop, s[q][kb], 0, 0, 0);
       }
       if (i + KLOOK < NK) kk[i + KLOOK] = ld8(kl + (((i + KLOOK) % KB) * 8 + (i + KLOOK) / KB) * 512);
+      if constexpr (C::QL) {
+        if (kb == KB - 1 && t + QLOOK < 8) qq[t + QLOOK] = ld8(qw + (t + QLOOK) * 512);
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
@@ -539,7 +577,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   // itself the compiler reads one or two operands ahead and waits on LDS
   // before the MFMA): +0.4-1.8% on the 480x832 segment and the 1280x704
   // history, same-run.
-  constexpr int NP = 8 * KB, VLOOK = 4;
+  constexpr int NP = 8 * KB, VLOOK = TIGHT ? HN_QLI_VLOOK : 4;
   auto vaddr = [&](int i) __attribute__((always_inline)) {
     const int kb = i / 8, t = (i / 4) % 2, c = i % 4;
     return vl + ((c * KB + kb) * 2 + t) * 512;
@@ -578,8 +616,9 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
 template <class C, int MIN_BLOCKS, bool HAS_I8>
 __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnParams p) {
   constexpr int QB = C::QB;
-  __shared__ Stage<C> stage0;
-  __shared__ Stage<C> stage1;
+  __shared__ __attribute__((aligned(4096))) Stage<C> stage0;
+  __shared__ __attribute__((aligned(4096))) Stage<C> stage1;
+  __shared__ QStore<C> qstore;
   const int task = (blockIdx.x & 7) * p.tasks_per_xcd + (blockIdx.x >> 3);
   if (task >= p.n_tasks) return;  // whole block leaves before any barrier
   const int h = task / p.n_tiles;
@@ -615,6 +654,16 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
         qreg[q][t] = __builtin_bit_cast(bf16x8, ld_b128(rq, (uint32_t)row[q] * q_tb + 16 * g, 32 * t));
   };
   load_q();
+  // QL: this wave's Q region and the lane's slot in its chunk 0; publish_q
+  // writes qreg there (only this wave reads it, so no barrier is needed)
+  const __bf16* qw = qstore.q + wave * 32 * D + lane * 8;
+  auto publish_q = [&]() __attribute__((always_inline)) {
+    if constexpr (C::QL) {
+      __bf16* qd = qstore.q + wave * 32 * D + lane * 8;
+#pragma unroll
+      for (int t = 0; t < 8; ++t) *reinterpret_cast<bf16x8*>(qd + t * 512) = qreg[0][t];
+    }
+  };
   Sources S;
   init_sources<C>(p, h, S);
 
@@ -700,8 +749,9 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
       sc_t[q] = F16 ? scale_h[q] : p.scale_log2;
     }
     const bool mask = (cur.nk < C::KT) || !rows_all;
-    if (mask) tile_math<C, true, F16, F16>(sc, qreg, acc, st, sc_t, cur.nk, row_ok);
-    else tile_math<C, false, F16, F16>(sc, qreg, acc, st, sc_t, cur.nk, row_ok);
+    constexpr bool TIGHT = C::QL && HAS_I8;
+    if (mask) tile_math<C, true, F16, F16, TIGHT>(sc, qreg, qw, acc, st, sc_t, cur.nk, row_ok);
+    else tile_math<C, false, F16, F16, TIGHT>(sc, qreg, qw, acc, st, sc_t, cur.nk, row_ok);
   };
   // One pipeline step: compute tile `cur` from stage `sc` while tile `nxt`
   // streams into stage `sn`; the stages alternate, unrolled by two so that
@@ -739,6 +789,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
     // to the start, to take every tile in bf16.
     if (have && cur.src < SRC_TXT) {
       to_f16_q();
+      publish_q();
       first_tile(std::integral_constant<int, 1>{});
       bool redo = false;
       while (have && cur.src < SRC_TXT) {
@@ -753,6 +804,7 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
       if (have || redo) {
         load_q();
         __builtin_amdgcn_s_waitcnt(0);
+        publish_q();
       }
       if (redo) {
         // start over: one softmax over every tile, INT8 ones staged in bf16
@@ -771,9 +823,11 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
         first_tile(std::integral_constant<int, I8_BF16>{});
       }
     } else {
+      publish_q();
       first_tile(std::integral_constant<int, I8_BF16>{});
     }
   } else {
+    publish_q();
     first_tile(std::integral_constant<int, I8_BF16>{});
   }
   // Phase 2: the bf16 tiles (and, after a restart, every tile)
@@ -899,12 +953,18 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
 #define HN_DENSE_KT 64
 #endif
 using DenseCfg = Cfg<HN_DENSE_NW, HN_DENSE_QB, HN_DENSE_KT>;
+// 384-row blocks: 12 waves x 32 rows (three per SIMD, <= 168 VGPRs, which
+// Q fits only in LDS: 96 KB beside the two 32 KB stages fills the CU's
+// 160 KB); waves 0-7 stage the tiles, so every SIMD has two staging waves.
+using Dense384Cfg = Cfg<12, 1, 64, true, 8>;
 using SparseCfg = Cfg<4, 1, 64>;
 static_assert(SparseCfg::ROWS == HN_TILE, "keep-list blocks must match the keep-list tile");
 
 }  // namespace
 
-int attn_dense_rows() { return DenseCfg::ROWS; }
+bool attn_rows_supported(int rows) {
+  return rows == DenseCfg::ROWS || rows == Dense384Cfg::ROWS || rows == SparseCfg::ROWS;
+}
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
   if (p.n_tasks == 0) return hipSuccess;
@@ -916,6 +976,13 @@ hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
     else
       hipLaunchKernelGGL((seg_attn_fwd_kernel<DenseCfg, HN_DENSE_MINB, false>), dim3(blocks), dim3(DenseCfg::T),
                          0, s, p);
+  } else if (p.tile_rows == Dense384Cfg::ROWS) {
+    if (p.has_i8)
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<Dense384Cfg, 1, true>), dim3(blocks), dim3(Dense384Cfg::T), 0, s,
+                         p);
+    else
+      hipLaunchKernelGGL((seg_attn_fwd_kernel<Dense384Cfg, 1, false>), dim3(blocks), dim3(Dense384Cfg::T), 0, s,
+                         p);
   } else if (p.tile_rows == SparseCfg::ROWS) {
     if (p.has_i8)
       hipLaunchKernelGGL((seg_attn_fwd_kernel<SparseCfg, 2, true>), dim3(blocks), dim3(SparseCfg::T), 0, s, p);

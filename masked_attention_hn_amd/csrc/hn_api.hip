@@ -180,21 +180,44 @@ int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, 
   return best;
 }
 
-// Query rows per tile of a plan: keep lists fix HN_TILE; dense plans use the
-// kernel's 256-row blocks (faster than 128-row ones even where 256-row blocks
-// leave compute units idle: in one run the 2-head share above took
-// 1.215-1.217 ms with 208 such blocks against 1.464 ms with 414 128-row
-// blocks, and 1.45-1.47 against 1.67-1.68 ms with its text queries).
-// opts->tile_rows = 128 gives the 128-row tiles (tuning, tests).
-int plan_tile_rows(bool sparse, const hn_plan_opts* o) {
-  if (sparse) return HN_TILE;
-  if (o && o->tile_rows == HN_TILE) return HN_TILE;
-  return hn::attn_dense_rows();
+// Query rows per tile of a dense plan: 256-row blocks (two waves per SIMD, Q
+// in registers) or 384-row ones (three waves per SIMD, Q in LDS), both one
+// block per CU.  A 384-row block stages (and dequantizes) each key tile for
+// 1.5x the rows, which measured 1% faster per row on the 480x832 segment,
+// 5% on the 1280x704 steady state and 7.5% on its 7th segment (INT8 history
+// dominant), same runs; but it has two thirds as many blocks to fill the
+// CUs with: the 2-head share took 1.613 ms with 138 384-row blocks against
+// 1.277 ms with 208 256-row ones.  The height taken is the one with the
+// smaller estimated makespan: rounds of blocks (with the key splits
+// choose_splits takes for it) x rows x (keys per split + 1,600
+// key-equivalents of per-block cost, the constant of the text-split model
+// below), a 384-row block's row-keys weighted 0.95.  Blocks of 256 rows
+// beat 128-row ones even where they leave CUs idle (the 2-head share:
+// 1.215-1.217 ms with 208 256-row blocks against 1.464 ms with 414 128-row
+// blocks, and 1.45-1.47 against 1.67-1.68 ms with its text queries), so 128
+// rows are taken only for keep lists, or when asked for (opts->tile_rows:
+// 128, 256 or 384 forces that height; tuning, tests).
+int choose_dense_rows(int H, int lq, int64_t keys_per_tile) {
+  const int64_t cus = device_cus();
+  int best_rows = 256;
+  double best_t = 0.0;
+  for (const int rows : {256, 384}) {
+    const int nq = (int)ceil_div(lq, rows);
+    const int sp = choose_splits(H, nq, keys_per_tile, 1);
+    const double rounds = (double)ceil_div((int64_t)H * nq * sp, cus);
+    const double t =
+        rounds * rows * ((double)keys_per_tile / sp + 1600.0) * (rows == 384 ? 0.95 : 1.0);
+    if (rows == 256 || t < best_t) {
+      best_t = t;
+      best_rows = rows;
+    }
+  }
+  return best_rows;
 }
 
 // A plan's query-tile height is one the attention kernel has an instance for.
 bool valid_tile_rows(int rows, bool sparse) {
-  return sparse ? rows == HN_TILE : (rows == HN_TILE || rows == hn::attn_dense_rows());
+  return sparse ? rows == HN_TILE : hn::attn_rows_supported(rows);
 }
 
 hn_status check_opts(const hn_plan_opts* o, bool sparse) {
@@ -203,9 +226,8 @@ hn_status check_opts(const hn_plan_opts* o, bool sparse) {
       o->n_splits_text > HN_MAX_SPLITS)
     return fail(HN_ERR_INVALID, "split counts %d / %d outside [0, %d]", o->n_splits, o->n_splits_text,
                 HN_MAX_SPLITS);
-  if (o->tile_rows != 0 && o->tile_rows != HN_TILE && o->tile_rows != hn::attn_dense_rows())
-    return fail(HN_ERR_INVALID, "tile_rows %d is not 0, %d or %d", o->tile_rows, HN_TILE,
-                hn::attn_dense_rows());
+  if (o->tile_rows != 0 && !hn::attn_rows_supported(o->tile_rows))
+    return fail(HN_ERR_INVALID, "tile_rows %d is not 0, 128, 256 or 384", o->tile_rows);
   if (sparse && o->tile_rows != 0 && o->tile_rows != HN_TILE)
     return fail(HN_ERR_INVALID, "a keep list fixes %d-row query tiles", HN_TILE);
   if (o->reserved0 != 0) return fail(HN_ERR_INVALID, "hn_plan_opts.reserved0 must be 0");
@@ -223,13 +245,15 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
   std::memset(pp, 0, sizeof(*pp));
   const int P = c->tokens_per_frame;
   const int lq = s->frames * P;
-  pp->tile_q = plan_tile_rows(sp != nullptr, opts);
+  const int kf = kept_frames(c);
+  if (sp) pp->tile_q = HN_TILE;
+  else if (opts && opts->tile_rows != 0) pp->tile_q = opts->tile_rows;
+  else pp->tile_q = choose_dense_rows(c->num_heads, lq, (int64_t)c->head_tokens + tl + (int64_t)kf * P + lq);
   pp->n_qtiles = (int)ceil_div(lq, pp->tile_q);
   pp->n_text_tiles = (int)ceil_div(tl, pp->tile_q);
   pp->lq = lq;
   pp->P = P;
   pp->head_tokens = c->head_tokens;
-  const int kf = kept_frames(c);
   pp->kept_frames = kf;
   pp->ring_tokens = kf * P;
   pp->ring_rot = (int)(((c->frames_seen - kf) % c->window_frames) * P);

@@ -223,7 +223,8 @@ struct CameraParams {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // Query rows per tile of a dense (keep-list free) plan; keep-list plans use HN_TILE.
-int attn_dense_rows();
+// query-tile heights the attention kernel has an instance for
+bool attn_rows_supported(int rows);
 
 // Launchers (defined next to their kernels); return the HIP error of the launch.
 hipError_t launch_quant_append(const AppendParams& p, hipStream_t s);

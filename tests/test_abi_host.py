@@ -137,13 +137,13 @@ def test_attention_rejects_stale_plan():
     out = [FAKE, None, None, None]  # o_vid, o_txt, lse, lse_txt
     call = lambda seg, pl, qq=q, oo=out, scale=0.1: fwd(ctypes.byref(c), ctypes.byref(seg.c), pl,
                                                         *qq, *kv, *oo, scale, None)
-    # dense plans come in the heights the kernel has instances for (128 and
-    # its default 256): a plan with one of them gets past the staleness check
-    # to the scale check
-    tiles = [t for t in (64, 128, 256, 512)
+    # dense plans come in the heights the kernel has instances for (128, 256
+    # and 384): a plan with one of them gets past the staleness check to the
+    # scale check
+    tiles = [t for t in (64, 128, 192, 256, 384, 512)
              if (setattr(plan, "tile_q", t), call(s, ctypes.byref(plan), scale=float("nan")))[1]
              == hn.HN_ERR_INVALID]
-    assert tiles == [128, 256]
+    assert tiles == [128, 256, 384]
     plan.sparse = 1                # a keep-list plan is always 128 rows
     plan.tile_q = 256
     assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
@@ -202,7 +202,7 @@ def test_split_count_forced_and_sized():
     spans = -(-(256 + vt * 6 * 32) // 256) * 256
     a256 = lambda b: -(-b // 256) * 256
     # partials for the dense plans' query-tile height R (the kernel's choice)
-    fits = [R for R in (64, 128, 256, 512)
+    fits = [R for R in (64, 128, 256, 384, 512)
             if n3 == spans + a256(2 * vt * R * 128 * 4) + a256(2 * vt * R * 4)]
     assert len(fits) == 1 and n3 > n1
     # out-of-range options are an error, not a silent fallback
@@ -226,11 +226,41 @@ def test_tile_rows_option():
     assert n_auto > 0 and n_128 > 0 and n_auto != n_128
 
 
+def test_dense_tile_height_follows_the_makespan_estimate():
+    """Without a device (256 compute units assumed): a dense plan takes 384-row
+    query tiles where their estimated makespan is smaller (the 480x832
+    segment: 496 blocks in 2 rounds against 736 in 3; the 1280x704 steady
+    state and its 7th segment, split in two either way), and 256-row ones
+    where 384-row blocks would leave more CUs idle (the 2-head share: 138
+    blocks against 208 in one round) or where the segment has at most 256
+    rows; a keep list fixes 128 rows."""
+
+    def heights(H, P, frames, W_, seen):
+        c = fake_cache(H=H, P=P, W=W_, cap=1 << 14)
+        c.frames_seen = seen
+        c.segments = 0
+        seg = hn.SegLayout(0, frames, P, 16, [], [], [])
+        auto = ws_size(c, seg, n_splits_text=1)
+        return [R for R in (128, 256, 384) if ws_size(c, seg, n_splits_text=1, tile_rows=R) == auto]
+
+    assert heights(16, 390, 30, 1, 0) == [384]        # 480x832 segment
+    assert heights(16, 880, 30, 18, 18) == [384]      # 1280x704 steady state
+    assert heights(16, 880, 30, 210, 180) == [384]    # its 7th segment (no window)
+    assert heights(2, 880, 30, 18, 18) == [256]       # 2-head share
+    # 240 rows of 1 head over a 24,000-key ring: one tile either way, split
+    # (so that the partial results, sized by the height, tell them apart)
+    assert heights(1, 120, 2, 200, 200) == [256]
+    c = fake_cache(H=16, P=390, W=1)
+    seg = hn.SegLayout(0, 30, 390, 16, [], [], [])
+    sp = hn.hn_block_sparse(128, 128, 92, 0, FAKE, FAKE)
+    assert ws_size(c, seg, sp) == ws_size(c, seg, sp, tile_rows=128) > 0
+
+
 def test_automatic_split_only_for_small_grids():
     """Without a device (256 compute units assumed) a 16-head grid with short
-    key lists is not split; a 1-head layout with 2 query tiles of long key
-    lists is split to about two blocks per CU, capped at 16 and at 1024 keys
-    per split."""
+    key lists (31 query tiles of 384 rows per head) is not split; a 1-head
+    layout with 2 query tiles of long key lists is split to about two blocks
+    per CU, capped at 16 and at 1024 keys per split."""
     plan_sizes = {}
     for H, P, frames, W_ in ((16, 390, 30, 1), (1, 128, 2, 200)):
         c = fake_cache(H=H, P=P, W=W_)
@@ -238,9 +268,9 @@ def test_automatic_split_only_for_small_grids():
         seg = hn.SegLayout(0, frames, P, 16, [], [], [])
         c.segments = 0
         plan_sizes[H] = ws_size(c, seg, n_splits_text=1)   # video tiles only here
-    # 16 heads x 92 (or 46) tiles: spans only (no partial results)
-    sizes = [-(-(-(-n_vt * 4 // 256) * 256 + n_vt * 4 * 32) // 256) * 256 for n_vt in (92 + 1, 46 + 1)]
-    assert plan_sizes[16] in sizes
+    # 16 heads x 31 tiles (+1 text tile): spans only (no partial results)
+    n_vt = 31 + 1
+    assert plan_sizes[16] == -(-(-(-n_vt * 4 // 256) * 256 + n_vt * 4 * 32) // 256) * 256
     # 1 head x 1-2 video tiles (+1 text tile): ring 25,600 + 16 + 256 keys -> 16 splits
     a256 = lambda b: -(-b // 256) * 256
     ok = []
@@ -266,7 +296,7 @@ def test_automatic_two_splits_fill_the_last_round():
         seg = hn.SegLayout(0, frames, P, 16, [], [], [])
         return ws_size(c, seg, n_splits=splits, n_splits_text=1)
 
-    steady = (16, 880, 30, 18)       # 1,664 blocks of 256 rows: 6.5 rounds
+    steady = (16, 880, 30, 18)       # 1,104 blocks of 384 rows: 4.3 rounds
     assert ws(*steady) == ws(*steady, splits=2) != ws(*steady, splits=1)
     short = (16, 390, 30, 1)         # 12,106 keys per query tile
     assert ws(*short) == ws(*short, splits=1)

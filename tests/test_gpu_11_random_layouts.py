@@ -51,7 +51,7 @@ def _layout(seed):
     w = W.Workload(f"rand{seed}", heads, segs, S, window, 500 + seed, kv_dist=dist, sparse_keep=keep,
                    sparse_seed=(900 + seed) if keep else None)
     # a keep list fixes 128-row query tiles
-    rows = int(rng.choice([0, 128] if keep else [0, 128, 256]))
+    rows = int(rng.choice([0, 128] if keep else [0, 128, 256, 384]))
     opts = hn.PlanOpts(n_splits=int(rng.choice([0, 1, 2, 3])), n_splits_text=int(rng.choice([0, 1, 2])),
                        tile_rows=rows)
     return w, opts

@@ -49,13 +49,16 @@ def _compare(w, d, run, rows, kv=None):
     assert np.all(np.isfinite(o))
 
 
-@pytest.mark.parametrize("rows", ["auto", "128"])
+@pytest.mark.parametrize("rows", ["auto", "128", "384"])
 @pytest.mark.parametrize("name", ["c1", "c1_evict", "c1_future", "m1", "m2", "m3", "m4"])
 def test_attention_small_all_rows(name, rows):
-    # dense plans use 256-row blocks; "128" forces the 128-row blocks (4 waves)
+    # small dense plans take 256-row blocks; "128" forces the 128-row blocks
+    # (4 waves), "384" the 384-row ones (12 waves, Q in LDS)
     print(f"[attn] {name} rows={rows}", flush=True)
     opts = None if rows == "auto" else hn.PlanOpts(tile_rows=int(rows))
     w = W.config(name)
+    if rows == "384" and w.sparse_keep is not None:
+        pytest.skip("a keep list fixes 128-row query tiles")
     d = data_of(name)
     run = G.Run(w, d, opts=opts)
     if rows != "auto" and w.sparse_keep is None:
@@ -75,13 +78,16 @@ def test_attention_full_size_sampled_rows(name):
         _DATA.pop(name)
 
 
-@pytest.mark.parametrize("name", ["c2", "c5"])
-def test_attention_full_size_all_rows(name):
-    # the 480x832 segment (dense and keep list): every one of its 11,700 rows
-    print(f"[attn] {name} all rows", flush=True)
+@pytest.mark.parametrize("name,rows", [("c2", "auto"), ("c2", "256"), ("c5", "auto")])
+def test_attention_full_size_all_rows(name, rows):
+    # the 480x832 segment (dense: 384-row tiles by default, also forced to
+    # 256; keep list): every one of its 11,700 rows
+    print(f"[attn] {name} all rows, rows={rows}", flush=True)
     w = W.config(name)
     d = data_of(name)
-    run = G.Run(w, d)
+    run = G.Run(w, d, opts=None if rows == "auto" else hn.PlanOpts(tile_rows=int(rows)))
+    if name == "c2":
+        assert run.plan.c.tile_q == (384 if rows == "auto" else int(rows))
     _compare(w, d, run, np.arange(w.current.video_len))
 
 

@@ -71,11 +71,13 @@ def _check(w, d, o, o_t, lse, lse_t, what):
     print(f"  {what}: max-abs video {err.max():.3e} text {err_t.max():.3e}", flush=True)
 
 
-@pytest.mark.parametrize("rows", ["auto", "128"])
+@pytest.mark.parametrize("rows", ["auto", "128", "384"])
 @pytest.mark.parametrize("name", ["c1", "m1", "m2", "m3"])
 def test_huge_queries(name, rows):
     print(f"[range] huge queries {name} rows={rows}", flush=True)
     w = W.config(name)
+    if rows == "384" and w.sparse_keep is not None:
+        pytest.skip("a keep list fixes 128-row query tiles")
     d = W.generate(w)
     opts = None if rows == "auto" else hn.PlanOpts(tile_rows=int(rows))
     run = G.Run(w, d, opts=opts)
@@ -104,7 +106,7 @@ PLACES = {
 }
 
 
-@pytest.mark.parametrize("rows", ["auto", "128"])
+@pytest.mark.parametrize("rows", ["auto", "128", "384"])
 @pytest.mark.parametrize("name,place", [(n, p) for n, ps in PLACES.items() for p in ps])
 def test_huge_history_key_restarts_in_bf16(name, place, rows):
     print(f"[range] huge key {name} {place} rows={rows}", flush=True)
