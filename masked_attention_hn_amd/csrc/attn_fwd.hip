@@ -748,7 +748,9 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   auto compute = [&](const Stage<C>& sc, auto f16_tag) __attribute__((always_inline)) {
     constexpr bool F16 = decltype(f16_tag)::value;
     const int wrows = 32 * QB;
-    const bool wave_live = (cur.r0 < wrow0 + wrows) && (cur.r1 > wrow0);
+    // waves whose rows all lie past the query set's end skip the math (a
+    // tile's last rows; full spans carry the row range [0, INT_MAX))
+    const bool wave_live = wrow0 < lq && (cur.r0 < wrow0 + wrows) && (cur.r1 > wrow0);
     if (!wave_live) return;
     const bool rows_all = (cur.r0 <= wrow0) && (cur.r1 >= wrow0 + wrows);
     bool row_ok[QB];
