@@ -248,7 +248,8 @@ typedef struct hn_plan_opts {
   int32_t n_splits;           /* key splits per video query tile: 0 = automatic, else 1 .. 16 */
   int32_t n_splits_text;      /* key splits per text query tile: 0 = automatic, else 1 .. 16 */
   int32_t tile_rows;          /* query rows per tile of a plan without keep list: 0 = automatic
-                                 (256), 128 or 256; plans with a keep list always use HN_TILE */
+                                 (256 or 384, see hn_tile_plan), 128, 256 or 384; plans with a
+                                 keep list always use HN_TILE */
   int32_t reserved0;          /* must be 0 */
 } hn_plan_opts;
 
@@ -269,8 +270,11 @@ typedef struct hn_plan_opts {
  * their own count: the one (of 1, 2, 4, 8, 16) with the least estimated
  * makespan when the blocks are dealt to the slots in order, so that they
  * fill what the video blocks leave free; tiles of fewer than 4096 keys stay
- * whole (opts->n_splits_text forces a count).  Dense plans use 256-row
- * query tiles (opts->tile_rows = 128 gives 128-row ones).  With n_splits > 1
+ * whole (opts->n_splits_text forces a count).  Dense plans use 256- or
+ * 384-row query tiles, whichever gives the smaller estimated makespan (the
+ * 384-row block stages each key tile for more rows but leaves more compute
+ * units idle on small grids); opts->tile_rows = 128, 256 or 384 forces a
+ * height.  With n_splits > 1
  * attention calls that share one plan workspace must not overlap in time
  * (same stream, or ordered), since they write its partial area. */
 typedef struct hn_tile_plan {
