@@ -48,6 +48,8 @@ def parse():
                     help="key splits per video query tile (0 = the library's automatic choice)")
     ap.add_argument("--text-splits", type=int, default=0,
                     help="key splits per text query tile (0 = automatic)")
+    ap.add_argument("--whole-tiles", type=int, default=0,
+                    help="with --splits > 1: leading video query tiles left unsplit (0 = every tile split)")
     ap.add_argument("--tile-rows", type=int, default=0,
                     help="query rows per tile of a plan without keep list: 128, 256 or 384 (0 = automatic)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -197,7 +199,8 @@ def main():
         csr = data["csr"]
         sparse = hn.BlockSparse(torch.from_numpy(csr["row_ptr"]), torch.from_numpy(csr["col"]),
                                 csr["n_qtiles"])
-    opts = hn.PlanOpts(n_splits=args.splits, n_splits_text=args.text_splits, tile_rows=args.tile_rows)
+    opts = hn.PlanOpts(n_splits=args.splits, n_splits_text=args.text_splits, tile_rows=args.tile_rows,
+                       whole_tiles=args.whole_tiles)
     ws = torch.empty(hn.hn_attn_workspace_size(cache, seg, sparse, opts), dtype=torch.uint8, device=dev)
     plan_c = hn.hn_tile_plan()
     plan = hn.Plan(ws, plan_c)
@@ -449,6 +452,10 @@ def main():
             "key_splits": args.splits or "automatic",
             "key_splits_text": args.text_splits or "automatic",
             "tile_rows": args.tile_rows or "automatic",
+            "whole_tiles": args.whole_tiles if args.splits else "automatic",
+            # what the plan of the timed launch took (text splits: of the joint launch)
+            "plan": {"tile_rows": plan_c.tile_q, "key_splits": plan_c.n_splits,
+                     "whole_tiles": plan_c.n_whole, "key_splits_text": plan_c.n_splits_text},
             "effective_flop_per_step": flops,
             "visible_pairs_per_head": pairs,
         },

@@ -250,7 +250,9 @@ typedef struct hn_plan_opts {
   int32_t tile_rows;          /* query rows per tile of a plan without keep list: 0 = automatic
                                  (256 or 384, see hn_tile_plan), 128, 256 or 384; plans with a
                                  keep list always use HN_TILE */
-  int32_t reserved0;          /* must be 0 */
+  int32_t whole_tiles;        /* with n_splits > 1 forced: leading video query tiles that run
+                                 unsplit (the others are split n_splits ways; >= n_qtiles: none
+                                 split); 0 = every tile split.  Must be 0 when n_splits < 2 */
 } hn_plan_opts;
 
 /* Tile plan for one (cache state, segment, keep list); filled by
@@ -260,12 +262,15 @@ typedef struct hn_plan_opts {
  * the video queries, tiles n_qtiles .. n_qtiles+n_text_tiles-1 the text
  * queries (head and tails).
  * Split-KV: when (heads x video query tiles) would leave the GPU's block
- * slots (one per compute unit for 256-row tiles, two for 128-row ones)
- * poorly filled, every query tile's keys are split into n_splits contiguous
+ * slots (one per compute unit for 256- and 384-row tiles, two for 128-row
+ * ones) poorly filled, query tiles' keys are split into n_splits contiguous
  * ranges that run as separate blocks; each writes a partial result into the
  * workspace and a merge kernel combines them (one softmax, exactly as
- * without the split up to rounding).  The split count comes from the
- * device's compute-unit count and the layout (opts->n_splits forces one).
+ * without the split up to rounding).  Either every video tile is split
+ * (n_whole = 0), or only the tiles from n_whole on, so that the whole tiles
+ * fill full rounds of blocks and the split pieces of the others the last
+ * one.  The choice comes from the device's compute-unit count and the
+ * layout (opts->n_splits and opts->whole_tiles force one).
  * Text query tiles, which follow all video tiles in a joint launch, get
  * their own count: the one (of 1, 2, 4, 8, 16) with the least estimated
  * makespan when the blocks are dealt to the slots in order, so that they
@@ -291,12 +296,14 @@ typedef struct hn_tile_plan {
   int64_t visible_pairs;      /* unmasked (video query, key) pairs per head; -1 if sparse */
   int64_t visible_pairs_text; /* unmasked (text query, key) pairs per head */
   int32_t n_splits_text;      /* key splits per text query tile, 1 .. 16 */
-  int32_t reserved0;
+  int32_t n_whole;            /* leading video query tiles that run unsplit when n_splits > 1
+                                 (0 .. n_qtiles-1); 0 when n_splits = 1 */
 } hn_tile_plan;
 
 /* Workspace bytes TILE_PLAN mode needs with the same opts (0 on invalid
- * arguments): the span lists, plus, with split-KV, H x tiles x splits x
- * tile_q x (128 + 1) floats of partial results. */
+ * arguments): the span lists, plus, with split-KV, H x (split tiles x
+ * splits, plus the text tiles' pieces) x tile_q x (128 + 1) floats of
+ * partial results. */
 size_t hn_attn_workspace_size(const hn_kv_cache* cache, const hn_seg_layout* seg,
                               const hn_block_sparse* sparse, const hn_plan_opts* opts);
 

@@ -69,7 +69,7 @@ class hn_block_sparse(ctypes.Structure):
 
 class hn_plan_opts(ctypes.Structure):
     _fields_ = [("n_splits", ctypes.c_int32), ("n_splits_text", ctypes.c_int32),
-                ("tile_rows", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
+                ("tile_rows", ctypes.c_int32), ("whole_tiles", ctypes.c_int32)]
 
 
 class hn_tile_plan(ctypes.Structure):
@@ -79,7 +79,7 @@ class hn_tile_plan(ctypes.Structure):
                 ("frames_seen", ctypes.c_int64), ("sparse", ctypes.c_int32),
                 ("n_splits", ctypes.c_int32), ("visible_pairs", ctypes.c_int64),
                 ("visible_pairs_text", ctypes.c_int64), ("n_splits_text", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32)]
+                ("n_whole", ctypes.c_int32)]
 
 
 class hn_kv_archive(ctypes.Structure):
@@ -328,9 +328,11 @@ def _sp(sparse: Optional[BlockSparse]):
     return ctypes.byref(sparse.c) if sparse is not None else None
 
 
-def PlanOpts(n_splits: int = 0, n_splits_text: int = 0, tile_rows: int = 0) -> hn_plan_opts:
-    """Plan choices for hn_attn_mask_build / hn_attn_workspace_size (0 = automatic)."""
-    return hn_plan_opts(n_splits, n_splits_text, tile_rows, 0)
+def PlanOpts(n_splits: int = 0, n_splits_text: int = 0, tile_rows: int = 0,
+             whole_tiles: int = 0) -> hn_plan_opts:
+    """Plan choices for hn_attn_mask_build / hn_attn_workspace_size (0 = automatic;
+    whole_tiles: with n_splits > 1, the leading video query tiles left unsplit)."""
+    return hn_plan_opts(n_splits, n_splits_text, tile_rows, whole_tiles)
 
 
 def _op(opts: Optional[hn_plan_opts]):

@@ -629,12 +629,24 @@ __global__ __launch_bounds__(C::T, MIN_BLOCKS) void seg_attn_fwd_kernel(AttnPara
   __shared__ __attribute__((aligned(4096))) Stage<C> stage0;
   __shared__ __attribute__((aligned(4096))) Stage<C> stage1;
   __shared__ QStore<C> qstore;
-  const int task = (blockIdx.x & 7) * p.tasks_per_xcd + (blockIdx.x >> 3);
-  if (task >= p.n_tasks) return;  // whole block leaves before any barrier
-  const int h = task / p.n_tiles;
-  const int vt = task - h * p.n_tiles;  // virtual tile: (query tile, key split), split fastest
+  // block b runs on XCD b % 8; its position b / 8 there picks a whole video
+  // tile first, then a split piece or text tile (head-major in each class)
+  const int xcd = blockIdx.x & 7, pos = blockIdx.x >> 3;
+  int h, vt;  // vt: virtual tile (query tile, key split), split fastest
+  if (pos < p.a_per_xcd) {
+    const int i = xcd * p.a_per_xcd + pos;
+    if (i >= p.a_tasks) return;  // whole block leaves before any barrier
+    h = i / p.n_whole;
+    vt = i - h * p.n_whole;
+  } else {
+    const int i = xcd * p.b_per_xcd + (pos - p.a_per_xcd);
+    if (i >= p.b_tasks) return;
+    const int nb = p.n_tiles - p.n_whole;
+    h = i / nb;
+    vt = p.n_whole + (i - h * nb);
+  }
   int tile, split_unused, n_split;
-  vt_decode(vt, p.n_qtiles, p.n_splits, p.n_splits_text, tile, split_unused, n_split);
+  vt_decode(vt, p.n_qtiles, p.n_whole, p.n_splits, p.n_splits_text, tile, split_unused, n_split);
   // plan tiles: video query tiles, then text query tiles (own head and tails)
   const bool text = tile >= p.n_qtiles;
   const int qt = text ? tile - p.n_qtiles : tile;  // tile within its query set
@@ -908,7 +920,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
   const int h = ht / p.n_tiles;
   const int t = ht - h * p.n_tiles;
   const bool text = t >= p.n_qtiles;
-  const int n_split = text ? p.n_splits_text : p.n_splits;
+  const int n_split = text ? p.n_splits_text : (t < p.n_whole ? 1 : p.n_splits);
   if (n_split == 1) return;  // this tile wrote its outputs directly
   const int qt = text ? t - p.n_qtiles : t;
   const int lq = text ? p.lq_txt : p.lq;
@@ -920,7 +932,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeParams p) {
     const int row = qt * p.tile_rows + rl;
     if (row >= lq) break;
     const int64_t base =
-        ((int64_t)h * p.n_pvt + (vt_first(t, p.n_qtiles, p.n_splits, p.n_splits_text) - p.part_vt0)) *
+        ((int64_t)h * p.n_pvt + (vt_first(t, p.n_qtiles, p.n_whole, p.n_splits, p.n_splits_text) - p.part_vt0)) *
             p.tile_rows + rl;
     float m = -INFINITY;
     for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, p.part_lse[base + (int64_t)sp * p.tile_rows]);
@@ -979,8 +991,8 @@ bool attn_rows_supported(int rows) {
 }
 
 hipError_t launch_attn(const AttnParams& p, hipStream_t s) {
-  if (p.n_tasks == 0) return hipSuccess;
-  const int blocks = 8 * p.tasks_per_xcd;
+  if (p.a_tasks + p.b_tasks == 0) return hipSuccess;
+  const int blocks = 8 * (p.a_per_xcd + p.b_per_xcd);
   if (p.tile_rows == DenseCfg::ROWS) {
     if (p.has_i8)
       hipLaunchKernelGGL((seg_attn_fwd_kernel<DenseCfg, HN_DENSE_MINB, true>), dim3(blocks), dim3(DenseCfg::T),

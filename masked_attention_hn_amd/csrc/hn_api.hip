@@ -101,10 +101,43 @@ int device_cus() {
   return n;
 }
 
-// Key splits per query tile (split-KV).  A split costs fp32 partial results,
-// a merge and one more first-tile latency per query tile: measured on MI355X
-// about a quarter of an unsplit task's time.  It pays where the grid leaves
-// the last round of blocks partly empty and half-length tasks fill it:
+// Per-block cost of the split models below, in key-equivalents on top of a
+// block's keys: Q load, first tile, partial write, share of the merge; a
+// constant fitted to same-run measurements of text splits.
+constexpr double kBlockOverhead = 1600.0;
+
+// Greedy list schedule: blocks dealt in order to the earliest free of the
+// slots; deal() adds `count` blocks of cost `cost`.
+struct SlotSim {
+  std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+  explicit SlotSim(int64_t slots) {
+    for (int64_t i = 0; i < slots; ++i) free_at.push(0.0);
+  }
+  void deal(int64_t count, double cost) {
+    for (int64_t i = 0; i < count; ++i) {
+      const double t = free_at.top();
+      free_at.pop();
+      free_at.push(t + cost);
+    }
+  }
+  double end() {
+    double t_end = 0.0;
+    while (!free_at.empty()) {
+      t_end = std::max(t_end, free_at.top());
+      free_at.pop();
+    }
+    return t_end;
+  }
+};
+
+// Key splits of the video query tiles (split-KV): n_whole leading tiles of
+// every head run whole, the others are split n_splits ways (n_whole = 0:
+// every tile split; n_splits = 1: none).  A split costs fp32 partial
+// results, a merge and one more first-tile latency.  With 384-row tiles the
+// hybrid below (64 of 69 tiles whole, the last 5 split in 3) against two
+// uniform splits, same runs: 1280x704 steady state 9.19 vs 9.62-9.75 ms,
+// its 7th segment 41.43-41.44 vs 42.31 ms.  Measured with 256-row tiles and
+// uniform splits:
 //   1280x704 steady state, 16 heads: 1,664 blocks of 256 rows = 6.5 rounds on
 //     256 CUs; 1 / 2 / 3 / 4 splits 10.22 / 9.60 / 10.48 / 9.95 ms per
 //     launch, and the 7th segment (158k INT8 history keys) 44.77 / 42.13 /
@@ -113,65 +146,99 @@ int device_cus() {
 //     1.270 / 1.380 / 1.384 / 1.466 ms;
 //   the 480x832 segment: 736 blocks, 2.9 rounds; 1 / 2 splits 1.059 /
 //     1.129 ms.
-// With r_s = rounds of the s-split grid, two splits are taken when
-// r_2 / 2 + 1/4 < r_1 and each half keeps at least 8192 keys.  A grid of at
-// most one block per two CUs is split to about one block per CU, with no
-// fewer than 1024 keys per split.  blocks_per_cu is how many blocks of the
-// plan's tile height share a CU.
-int choose_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu) {
+// A grid of at most one block per two CUs is split to about one block per
+// CU, with no fewer than 1024 keys per split.  Larger grids take, of
+//   unsplit; two uniform splits (each half keeping >= 8192 keys); and the
+//   hybrid: the whole tiles fill as many full rounds as they can, and the
+//   last T tiles of every head (T x H >= the tasks left over) are split in
+//   s = slots / (T x H) pieces (>= 2, >= 1024 keys each), which fill one
+//   last round,
+// the one with the least makespan when the blocks are dealt in order to the
+// earliest free slot (whole tiles first, as the kernel dispatches them),
+// each costing its keys plus kBlockOverhead.  blocks_per_cu is how many
+// blocks of the plan's tile height share a CU.
+struct VideoSplit {
+  int n_splits = 1, n_whole = 0;
+  double makespan = 0.0;  // key-equivalents per slot
+};
+VideoSplit choose_video_splits(int H, int n_qtiles, int64_t keys_per_tile, int blocks_per_cu) {
+  VideoSplit best;
   const int64_t cus = device_cus();
   const int64_t tasks = (int64_t)H * n_qtiles;
-  if (tasks <= 0) return 1;
+  if (tasks <= 0) return best;
+  const double keys = (double)keys_per_tile;
   if (2 * tasks <= cus) {
     int64_t sp = ceil_div(cus, tasks);
     sp = std::min<int64_t>(sp, keys_per_tile / 1024);
     sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
-    return (int)std::max<int64_t>(sp, 1);
+    best.n_splits = (int)std::max<int64_t>(sp, 1);
+    best.makespan = keys / best.n_splits + kBlockOverhead;
+    return best;
   }
   const int64_t slots = cus * std::max(blocks_per_cu, 1);
-  const int64_t r1 = ceil_div(tasks, slots), r2 = ceil_div(2 * tasks, slots);
-  if (keys_per_tile >= 16384 && 2 * r2 + 1 < 4 * r1) return 2;
-  return 1;
+  auto uniform = [&](int sp) {
+    return (double)ceil_div(tasks * sp, slots) * (keys / sp + kBlockOverhead);
+  };
+  best.makespan = uniform(1);
+  if (keys_per_tile >= 16384 && uniform(2) < best.makespan) {
+    best.n_splits = 2;
+    best.makespan = uniform(2);
+  }
+  const int64_t rest = tasks % slots;
+  if (rest > 0) {
+    const int64_t T = ceil_div(rest, H);  // split tiles per head
+    const int64_t pieces = T * H;
+    int64_t sp = std::min<int64_t>(slots / pieces, keys_per_tile / 1024);
+    sp = std::min<int64_t>(sp, HN_MAX_SPLITS);
+    if (T < n_qtiles && sp >= 2) {
+      SlotSim sim(slots);
+      sim.deal(tasks - pieces, keys + kBlockOverhead);
+      sim.deal(pieces * sp, keys / sp + kBlockOverhead);
+      const double t = sim.end();
+      if (t < best.makespan) {
+        best.n_splits = (int)sp;
+        best.n_whole = (int)(n_qtiles - T);
+        best.makespan = t;
+      }
+    }
+  }
+  return best;
 }
 
 // Key splits per text query tile.  The text tiles of a joint launch run after
 // the video tiles and fill what the video blocks leave of the last round, or
 // rounds of their own.  The count taken is the one whose estimated makespan is
 // least when the blocks are dealt in order to the earliest free slot (the
-// video blocks first, all of one size, then the text pieces), each block
-// costing its keys plus a fixed 1,600 key-equivalents (Q load, first tile,
-// partial write, share of the merge), a constant fitted to same-run
-// measurements: 4 splits on the 480x832 segment, where the video leaves 32 of
-// 256 slots free in its last round, and 8 on the 1280x704 one, where it fills
-// its last round (joint launch 2.5% faster than with 4); ties go to the fewer
-// splits (the 2-head share's 10 text tiles run whole beside its 208 video
-// blocks).  Text tiles with
-// fewer than 4096 keys are not split, and pieces keep at least 1,024 keys.
-int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, int n_text_tiles,
-                       int64_t keys_per_tile, int blocks_per_cu) {
+// video blocks first, as choose_video_splits laid them out, then the text
+// pieces), each block costing its keys plus kBlockOverhead, a constant fitted
+// to same-run measurements with 256-row tiles and uniformly split video: 4
+// splits on the 480x832 segment, where the video left 32 of 256 slots free
+// in its last round, and 8 on the 1280x704 one, where it filled its last
+// round (joint launch 2.5% faster than with 4).  With 384-row tiles it takes
+// 4 on both (the 1280x704 video now ends in split pieces): same-run joint
+// launches within 0.7% of 8 either way (9.83-9.87 vs 9.80 ms; the 7th
+// segment 43.59-43.66 vs 43.70 ms).  Ties go to the fewer splits (the
+// 2-head share's 10 text tiles run whole beside its 208 video blocks).
+// Text tiles with fewer than 4096 keys are not split, and pieces keep at
+// least 1,024 keys.
+int choose_text_splits(int H, const VideoSplit& v, int n_qtiles, int64_t video_keys_per_tile,
+                       int n_text_tiles, int64_t keys_per_tile, int blocks_per_cu) {
   if (n_text_tiles <= 0 || keys_per_tile < 4096) return 1;
-  constexpr double kOverhead = 1600.0;
   const int64_t slots = std::max<int64_t>(device_cus() * std::max(blocks_per_cu, 1), 1);
-  const int64_t q = video_tasks / slots, r = video_tasks % slots;
-  const double kv = (double)video_keys_per_task + kOverhead;
+  const double kv = (double)video_keys_per_tile;
   int best = 1;
   double best_t = 0.0;
   for (int sp = 1; sp <= HN_MAX_SPLITS; sp *= 2) {
     if (sp > 1 && keys_per_tile / sp < 1024) break;
-    std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
-    for (int64_t i = 0; i < slots; ++i) free_at.push((double)(q + (i < r ? 1 : 0)) * kv);
-    const double kt = (double)keys_per_tile / sp + kOverhead;
-    const int64_t pieces = (int64_t)H * n_text_tiles * sp;
-    for (int64_t i = 0; i < pieces; ++i) {
-      const double t = free_at.top();
-      free_at.pop();
-      free_at.push(t + kt);
+    SlotSim sim(slots);
+    if (v.n_splits == 1) {
+      sim.deal((int64_t)H * n_qtiles, kv + kBlockOverhead);
+    } else {
+      sim.deal((int64_t)H * v.n_whole, kv + kBlockOverhead);
+      sim.deal((int64_t)H * (n_qtiles - v.n_whole) * v.n_splits, kv / v.n_splits + kBlockOverhead);
     }
-    double t_end = 0.0;
-    while (!free_at.empty()) {
-      t_end = std::max(t_end, free_at.top());
-      free_at.pop();
-    }
+    sim.deal((int64_t)H * n_text_tiles * sp, (double)keys_per_tile / sp + kBlockOverhead);
+    const double t_end = sim.end();
     if (sp == 1 || t_end < best_t * (1.0 - 1e-9)) {
       best_t = t_end;
       best = sp;
@@ -188,25 +255,19 @@ int choose_text_splits(int H, int64_t video_tasks, int64_t video_keys_per_task, 
 // dominant), same runs; but it has two thirds as many blocks to fill the
 // CUs with: the 2-head share took 1.613 ms with 138 384-row blocks against
 // 1.277 ms with 208 256-row ones.  The height taken is the one with the
-// smaller estimated makespan: rounds of blocks (with the key splits
-// choose_splits takes for it) x rows x (keys per split + 1,600
-// key-equivalents of per-block cost, the constant of the text-split model
-// below), a 384-row block's row-keys weighted 0.95.  Blocks of 256 rows
-// beat 128-row ones even where they leave CUs idle (the 2-head share:
+// smaller estimated makespan: choose_video_splits' makespan for it x rows,
+// a 384-row block's row-keys weighted 0.95.  Blocks of 256 rows beat
+// 128-row ones even where they leave CUs idle (the 2-head share:
 // 1.215-1.217 ms with 208 256-row blocks against 1.464 ms with 414 128-row
 // blocks, and 1.45-1.47 against 1.67-1.68 ms with its text queries), so 128
 // rows are taken only for keep lists, or when asked for (opts->tile_rows:
 // 128, 256 or 384 forces that height; tuning, tests).
 int choose_dense_rows(int H, int lq, int64_t keys_per_tile) {
-  const int64_t cus = device_cus();
   int best_rows = 256;
   double best_t = 0.0;
   for (const int rows : {256, 384}) {
     const int nq = (int)ceil_div(lq, rows);
-    const int sp = choose_splits(H, nq, keys_per_tile, 1);
-    const double rounds = (double)ceil_div((int64_t)H * nq * sp, cus);
-    const double t =
-        rounds * rows * ((double)keys_per_tile / sp + 1600.0) * (rows == 384 ? 0.95 : 1.0);
+    const double t = choose_video_splits(H, nq, keys_per_tile, 1).makespan * rows * (rows == 384 ? 0.95 : 1.0);
     if (rows == 256 || t < best_t) {
       best_t = t;
       best_rows = rows;
@@ -230,7 +291,9 @@ hn_status check_opts(const hn_plan_opts* o, bool sparse) {
     return fail(HN_ERR_INVALID, "tile_rows %d is not 0, 128, 256 or 384", o->tile_rows);
   if (sparse && o->tile_rows != 0 && o->tile_rows != HN_TILE)
     return fail(HN_ERR_INVALID, "a keep list fixes %d-row query tiles", HN_TILE);
-  if (o->reserved0 != 0) return fail(HN_ERR_INVALID, "hn_plan_opts.reserved0 must be 0");
+  if (o->whole_tiles < 0 || (o->whole_tiles != 0 && o->n_splits < 2))
+    return fail(HN_ERR_INVALID, "whole_tiles %d needs a forced split count > 1 (n_splits %d)", o->whole_tiles,
+                o->n_splits);
   return HN_OK;
 }
 
@@ -275,17 +338,26 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
     int64_t keys = (int64_t)pp->head_tokens + tl;
     int64_t video = (int64_t)pp->ring_tokens + lq;
     if (sp && sp->row_ptr && pp->n_qtiles > 0) video = video / 4;
-    // dense 256-row blocks run one per CU, 128-row blocks two
-    pp->n_splits = (opts && opts->n_splits > 0)
-                       ? opts->n_splits
-                       : choose_splits(c->num_heads, pp->n_qtiles, keys + video, pp->tile_q >= 256 ? 1 : 2);
-    // text queries see heads, the whole ring and the own video (no keep list)
+    // dense 256- and 384-row blocks run one per CU, 128-row blocks two
     const int bpc = pp->tile_q >= 256 ? 1 : 2;
+    VideoSplit v;
+    if (opts && opts->n_splits > 0) {
+      v.n_splits = opts->n_splits;
+      v.n_whole = opts->whole_tiles;
+    } else {
+      v = choose_video_splits(c->num_heads, pp->n_qtiles, keys + video, bpc);
+    }
+    // canonical form: n_whole = 0 without a split; a split of no tile is none
+    if (v.n_splits == 1 || v.n_whole >= pp->n_qtiles) {
+      v.n_splits = 1;
+      v.n_whole = 0;
+    }
+    pp->n_splits = v.n_splits;
+    pp->n_whole = v.n_whole;
+    // text queries see heads, the whole ring and the own video (no keep list)
     pp->n_splits_text = (opts && opts->n_splits_text > 0)
                             ? opts->n_splits_text
-                            : choose_text_splits(c->num_heads,
-                                                 (int64_t)c->num_heads * pp->n_qtiles * pp->n_splits,
-                                                 (keys + video) / pp->n_splits, pp->n_text_tiles,
+                            : choose_text_splits(c->num_heads, v, pp->n_qtiles, keys + video, pp->n_text_tiles,
                                                  keys + (int64_t)pp->ring_tokens + lq, bpc);
   }
   int max_spans = 4 + s->num_actions;
@@ -307,16 +379,17 @@ hn_status make_plan_params(const hn_kv_cache* c, const hn_seg_layout* s, const h
 }
 
 int plan_vt(const hn::PlanParams& pp) {
-  return hn::vt_count(pp.n_qtiles, pp.n_text_tiles, pp.n_splits, pp.n_splits_text);
+  return hn::vt_count(pp.n_qtiles, pp.n_text_tiles, pp.n_whole, pp.n_splits, pp.n_splits_text);
 }
 
-// Virtual tiles with a partial-result slot: [part_vt0, n_vt) -- every one when
-// video tiles are split, the text tiles when only they are, none otherwise.
-void plan_partials(int n_qtiles, int n_text_tiles, int ns, int nst, int* part_vt0, int* n_pvt) {
-  const int n_vt = hn::vt_count(n_qtiles, n_text_tiles, ns, nst);
+// Virtual tiles with a partial-result slot: [part_vt0, n_vt) -- from the first
+// split video tile on when video tiles are split, the text tiles when only
+// they are, none otherwise.
+void plan_partials(int n_qtiles, int n_text_tiles, int nw, int ns, int nst, int* part_vt0, int* n_pvt) {
+  const int n_vt = hn::vt_count(n_qtiles, n_text_tiles, nw, ns, nst);
   if (ns > 1) {
-    *part_vt0 = 0;
-    *n_pvt = n_vt;
+    *part_vt0 = nw;
+    *n_pvt = n_vt - nw;
   } else if (nst > 1 && n_text_tiles > 0) {
     *part_vt0 = n_qtiles;
     *n_pvt = n_vt - n_qtiles;
@@ -328,7 +401,7 @@ void plan_partials(int n_qtiles, int n_text_tiles, int ns, int nst, int* part_vt
 
 size_t plan_ws_bytes(const hn_kv_cache* c, const hn::PlanParams& pp) {
   int v0 = 0, np = 0;
-  plan_partials(pp.n_qtiles, pp.n_text_tiles, pp.n_splits, pp.n_splits_text, &v0, &np);
+  plan_partials(pp.n_qtiles, pp.n_text_tiles, pp.n_whole, pp.n_splits, pp.n_splits_text, &v0, &np);
   return hn::plan_bytes(c->num_heads, plan_vt(pp), pp.max_spans, pp.tile_q, np);
 }
 
@@ -397,7 +470,7 @@ void fill_plan(const hn::PlanParams& pp, const hn_kv_cache* c, const hn_seg_layo
   plan->sparse = pp.sparse;
   plan->n_splits = pp.n_splits;
   plan->n_splits_text = pp.n_splits_text;
-  plan->reserved0 = 0;
+  plan->n_whole = pp.n_whole;
   {
     // text queries: every text row sees heads, ring, own head and own
     // video; a tail row also sees its own tail
@@ -465,7 +538,8 @@ hn_status attn_prepare(const hn_kv_cache* c, const hn_seg_layout* s, const hn_ti
       plan->head_tokens != c->head_tokens || !valid_tile_rows(tq, plan->sparse != 0) ||
       plan->n_qtiles != (int)ceil_div(lq, tq) || plan->n_text_tiles != (int)ceil_div(tl, tq) ||
       plan->n_splits < 1 || plan->n_splits > HN_MAX_SPLITS || plan->n_splits_text < 1 ||
-      plan->n_splits_text > HN_MAX_SPLITS)
+      plan->n_splits_text > HN_MAX_SPLITS || plan->n_whole < 0 ||
+      (plan->n_splits == 1 ? plan->n_whole != 0 : plan->n_whole >= plan->n_qtiles))
     return fail(HN_ERR_ORDER, "tile plan was built for another cache state or segment");
   if (!q_vid || !k_vid || !v_vid || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o video pointer is NULL");
   if (tl > 0 && (!k_txt || !v_txt)) return fail(HN_ERR_NULL, "k_txt/v_txt is NULL");
@@ -489,16 +563,21 @@ hn_status attn_prepare(const hn_kv_cache* c, const hn_seg_layout* s, const hn_ti
   p.n_qtiles = plan->n_qtiles;
   p.n_splits = plan->n_splits;
   p.n_splits_text = plan->n_splits_text;
-  p.n_vt = hn::vt_count(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text);
-  p.n_tiles = hn::vt_count(plan->n_qtiles, text_q ? plan->n_text_tiles : 0, plan->n_splits, plan->n_splits_text);
+  p.n_whole = plan->n_whole;
+  p.n_vt = hn::vt_count(plan->n_qtiles, plan->n_text_tiles, p.n_whole, plan->n_splits, plan->n_splits_text);
+  p.n_tiles = hn::vt_count(plan->n_qtiles, text_q ? plan->n_text_tiles : 0, p.n_whole, plan->n_splits,
+                           plan->n_splits_text);
   // partial results exist iff some launched tile is split
   const bool partials = plan->n_splits > 1 || (text_q && plan->n_splits_text > 1);
-  plan_partials(plan->n_qtiles, plan->n_text_tiles, plan->n_splits, plan->n_splits_text, &p.part_vt0,
+  plan_partials(plan->n_qtiles, plan->n_text_tiles, p.n_whole, plan->n_splits, plan->n_splits_text, &p.part_vt0,
                 &p.n_pvt);
   p.tile_rows = plan->tile_q;
   p.max_spans = plan->max_spans;
-  p.n_tasks = p.H * p.n_tiles;
-  p.tasks_per_xcd = (p.n_tasks + 7) / 8;
+  // whole video tiles first on every XCD, then the rest (see AttnParams)
+  p.a_tasks = p.H * p.n_whole;
+  p.a_per_xcd = (p.a_tasks + 7) / 8;
+  p.b_tasks = p.H * (p.n_tiles - p.n_whole);
+  p.b_per_xcd = (p.b_tasks + 7) / 8;
   p.head_cap = c->head_cap_tokens;
   p.ring_cap = c->window_frames * P;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
@@ -532,6 +611,7 @@ hn_status attn_prepare(const hn_kv_cache* c, const hn_seg_layout* s, const hn_ti
     std::memset(&m, 0, sizeof(m));
     m.H = p.H;
     m.n_splits = p.n_splits;
+    m.n_whole = p.n_whole;
     m.n_splits_text = p.n_splits_text;
     m.part_vt0 = p.part_vt0;
     m.n_pvt = p.n_pvt;

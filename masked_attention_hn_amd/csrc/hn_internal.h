@@ -35,7 +35,8 @@ static_assert(sizeof(Span) == 32, "Span layout");
 struct PlanParams {
   int32_t n_qtiles;      // video query tiles
   int32_t n_text_tiles;  // text query tiles, after the video tiles
-  int32_t n_splits;      // key-range splits per video query tile (split-KV); 1 = none
+  int32_t n_splits;      // key-range splits per split video query tile (split-KV); 1 = none
+  int32_t n_whole;       // leading video query tiles that run unsplit (0 if n_splits == 1)
   int32_t n_splits_text; // key-range splits per text query tile
   int32_t tile_q;
   int32_t lq;            // F*P video queries
@@ -64,8 +65,8 @@ struct PlanParams {
 // split, split fastest): int32 count[n_vt] padded to 256 bytes, then
 // Span spans[n_vt][max_spans]; with splits, then (256-byte aligned) the
 // partial results float o[H][n_pvt][rows][D] and float lse[H][n_pvt][rows]
-// of the n_pvt virtual tiles from part_vt0 on (every virtual tile when video
-// tiles are split, else only the text tiles).
+// of the n_pvt virtual tiles from part_vt0 on (from the first split video
+// tile on when video tiles are split, else only the text tiles).
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 inline size_t plan_counts_bytes(int n_vt) { return align256((size_t)n_vt * sizeof(int32_t)); }
 inline size_t plan_spans_bytes(int n_vt, int max_spans) {
@@ -83,22 +84,32 @@ inline size_t plan_bytes(int H, int n_vt, int max_spans, int rows, int n_pvt) {
   return b;
 }
 
-// Virtual tiles: every video query tile split ns ways, then every text query
-// tile split nst ways, split index fastest.
-__host__ __device__ inline int vt_count(int n_qtiles, int n_text_tiles, int ns, int nst) {
-  return n_qtiles * ns + n_text_tiles * nst;
+// Virtual tiles: the first nw video query tiles whole, the other video query
+// tiles split ns ways, then every text query tile split nst ways, split
+// index fastest.  (nw = 0: every video tile split ns ways.)
+__host__ __device__ inline int vt_video(int n_qtiles, int nw, int ns) { return nw + (n_qtiles - nw) * ns; }
+__host__ __device__ inline int vt_count(int n_qtiles, int n_text_tiles, int nw, int ns, int nst) {
+  return vt_video(n_qtiles, nw, ns) + n_text_tiles * nst;
 }
-__host__ __device__ inline int vt_first(int tile, int n_qtiles, int ns, int nst) {
-  return tile < n_qtiles ? tile * ns : n_qtiles * ns + (tile - n_qtiles) * nst;
+__host__ __device__ inline int vt_first(int tile, int n_qtiles, int nw, int ns, int nst) {
+  if (tile < nw) return tile;
+  if (tile < n_qtiles) return nw + (tile - nw) * ns;
+  return vt_video(n_qtiles, nw, ns) + (tile - n_qtiles) * nst;
 }
-__host__ __device__ inline void vt_decode(int vt, int n_qtiles, int ns, int nst, int& tile, int& split,
+__host__ __device__ inline void vt_decode(int vt, int n_qtiles, int nw, int ns, int nst, int& tile, int& split,
                                           int& n_split) {
-  if (vt < n_qtiles * ns) {
-    tile = vt / ns;
-    split = vt - tile * ns;
+  const int nv = vt_video(n_qtiles, nw, ns);
+  if (vt < nw) {
+    tile = vt;
+    split = 0;
+    n_split = 1;
+  } else if (vt < nv) {
+    const int r = vt - nw;
+    tile = nw + r / ns;
+    split = r - (r / ns) * ns;
     n_split = ns;
   } else {
-    const int r = vt - n_qtiles * ns;
+    const int r = vt - nv;
     tile = n_qtiles + r / nst;
     split = r - (r / nst) * nst;
     n_split = nst;
@@ -110,7 +121,8 @@ struct AttnParams {
   int32_t lq;            // video query rows
   int32_t n_qtiles;      // video query tiles
   int32_t n_tiles;       // virtual tiles per head this launch covers (video, then text if any)
-  int32_t n_splits;      // key splits per video query tile; > 1: write partials, merge after
+  int32_t n_splits;      // key splits per split video query tile; > 1: write partials, merge after
+  int32_t n_whole;       // leading video query tiles that run unsplit
   int32_t n_splits_text; // key splits per text query tile
   int32_t n_vt;          // virtual tiles per head in the plan
   int32_t part_vt0;      // first virtual tile with a partial-result slot
@@ -118,8 +130,13 @@ struct AttnParams {
   int32_t lq_txt;        // text query rows
   int32_t tile_rows;     // query rows per plan tile (selects the kernel instance)
   int32_t max_spans;
-  int32_t n_tasks;
-  int32_t tasks_per_xcd;
+  // Blocks come in two classes, each spread evenly over the 8 XCDs and the
+  // first dispatched first on every XCD: the whole video tiles (virtual
+  // tiles [0, n_whole) of every head), then the rest ([n_whole, n_tiles):
+  // split video tiles, text tiles), so that the split pieces fill the last
+  // round.  With n_whole = 0 there is only the second class.
+  int32_t a_tasks, a_per_xcd;
+  int32_t b_tasks, b_per_xcd;
   int32_t head_cap;      // head-store stride (tokens) per head
   int32_t ring_cap;      // ring stride (tokens) per head = W*P
   float scale_log2;      // sm_scale * log2(e)
@@ -153,6 +170,7 @@ struct AttnParams {
 struct MergeParams {
   int32_t H;
   int32_t n_splits;
+  int32_t n_whole;
   int32_t n_splits_text;
   int32_t part_vt0;      // first virtual tile with a partial-result slot
   int32_t n_pvt;         // partial-result slots per head

@@ -25,9 +25,10 @@
 // and they attend densely (keep lists concern video query tiles): at most
 // 4 + m spans as well.
 //
-// Split-KV: with n_splits > 1 every video query tile (n_splits_text > 1: every
-// text query tile) becomes that many virtual tiles (split fastest), each the
-// same span list clipped to one contiguous range
+// Split-KV: with n_splits > 1 every video query tile from n_whole on (the
+// first n_whole run whole; n_splits_text > 1: every text query tile) becomes
+// that many virtual tiles (split fastest), each the same span list clipped
+// to one contiguous range
 // of its keys in visiting order, with range boundaries on multiples of 64
 // keys; the attention kernel writes partial results for each and a merge
 // kernel combines them.
@@ -196,7 +197,7 @@ __device__ int64_t split_bound(int64_t total, int i, int n) {
 // the tile's keys, then the spans clipped to this split's range.
 __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
   int qt, split, n_split;
-  vt_decode(vt, p.n_qtiles, p.n_splits, p.n_splits_text, qt, split, n_split);
+  vt_decode(vt, p.n_qtiles, p.n_whole, p.n_splits, p.n_splits_text, qt, split, n_split);
   if (n_split == 1) return build_tile_spans(p, qt, out);
   int64_t total = 0;
   build_tile_spans(p, qt, nullptr, 0, INT64_MAX, &total);
@@ -208,13 +209,13 @@ __device__ int build_spans(const PlanParams& p, int vt, Span* out) {
 // wave walks both the video and the text span builder one after the other.
 __global__ __launch_bounds__(64) void plan_kernel(PlanParams p, int32_t* counts, Span* spans) {
   const int i = blockIdx.x * 64 + threadIdx.x;
-  const int n_vid = p.n_qtiles * p.n_splits;
+  const int n_vid = vt_video(p.n_qtiles, p.n_whole, p.n_splits);
   const int pad = (n_vid + 63) & ~63;
   int vt;
   if (i < n_vid) vt = i;
   else if (i < pad) return;
   else vt = n_vid + (i - pad);
-  if (vt >= vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text)) return;
+  if (vt >= vt_count(p.n_qtiles, p.n_text_tiles, p.n_whole, p.n_splits, p.n_splits_text)) return;
   counts[vt] = build_spans(p, vt, spans + (int64_t)vt * p.max_spans);
 }
 
@@ -263,9 +264,9 @@ __global__ __launch_bounds__(256) void dense_kernel(DenseParams d) {
 
 hipError_t launch_plan(const PlanParams& p, void* workspace, hipStream_t s) {
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
-  const int n_vt = vt_count(p.n_qtiles, p.n_text_tiles, p.n_splits, p.n_splits_text);
+  const int n_vt = vt_count(p.n_qtiles, p.n_text_tiles, p.n_whole, p.n_splits, p.n_splits_text);
   Span* spans = reinterpret_cast<Span*>(reinterpret_cast<char*>(workspace) + plan_counts_bytes(n_vt));
-  const int n_vid = p.n_qtiles * p.n_splits;
+  const int n_vid = vt_video(p.n_qtiles, p.n_whole, p.n_splits);
   const int threads = ((n_vid + 63) & ~63) + (n_vt - n_vid);
   const int blocks = (threads + 63) / 64;
   if (blocks == 0) return hipSuccess;

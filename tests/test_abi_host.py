@@ -182,9 +182,9 @@ def test_cache_sizes():
         hn.hn_kv_cache_sizes(0, 18, 880, 0)
 
 
-def ws_size(c, seg, sparse=None, n_splits=0, n_splits_text=0, tile_rows=0):
+def ws_size(c, seg, sparse=None, n_splits=0, n_splits_text=0, tile_rows=0, whole_tiles=0):
     """hn_attn_workspace_size with plan options (0 = automatic)."""
-    opts = hn.PlanOpts(n_splits, n_splits_text, tile_rows)
+    opts = hn.PlanOpts(n_splits, n_splits_text, tile_rows, whole_tiles)
     return hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(seg.c),
                                           ctypes.byref(sparse) if sparse is not None else None,
                                           ctypes.byref(opts))
@@ -209,12 +209,34 @@ def test_split_count_forced_and_sized():
     assert ws_size(c, s, n_splits=17) == 0 and "split counts" in hn.hn_last_error()
     assert ws_size(c, s, n_splits_text=-1) == 0
     assert ws_size(c, s, tile_rows=64) == 0 and "tile_rows" in hn.hn_last_error()
-    bad = hn.PlanOpts()
-    bad.reserved0 = 1
-    assert hn._lib.hn_attn_workspace_size(ctypes.byref(c), ctypes.byref(s.c), None, ctypes.byref(bad)) == 0
+    # whole_tiles only with a forced split count > 1, and not negative
+    assert ws_size(c, s, whole_tiles=1) == 0 and "whole_tiles" in hn.hn_last_error()
+    assert ws_size(c, s, n_splits=1, whole_tiles=1) == 0
+    assert ws_size(c, s, n_splits=3, whole_tiles=-1) == 0
     sp = hn.hn_block_sparse(128, 128, 1, 0, FAKE, FAKE)
     assert ws_size(c, s, sp, tile_rows=128) > 0
     assert ws_size(c, s, sp, tile_rows=fits[0]) == (0 if fits[0] != 128 else ws_size(c, s, sp))
+
+
+def test_whole_tiles_sized():
+    """With whole_tiles = w the first w video query tiles run whole and the
+    others split: w + (n_qtiles - w) x splits video virtual tiles, partial
+    results for the split ones and the text tiles (here one text tile);
+    w >= n_qtiles means no split at all."""
+    c = fake_cache(H=2, P=24, W=4, cap=48)
+    s = hn.SegLayout(0, 30, 24, 16, [8, 8], [0, 15], [15, 30])     # 720 video rows, 32 text rows
+    a256 = lambda b: -(-b // 256) * 256
+    R = 256
+    nq = 3
+    for w in (0, 1, 2):
+        vt = w + (nq - w) * 3 + 1
+        n_pvt = vt - w
+        spans = a256(a256(vt * 4) + vt * 6 * 32)
+        want = spans + a256(2 * n_pvt * R * 128 * 4) + a256(2 * n_pvt * R * 4)
+        assert ws_size(c, s, n_splits=3, n_splits_text=1, tile_rows=R, whole_tiles=w) == want
+    # every tile whole: the plan of no split
+    assert (ws_size(c, s, n_splits=3, n_splits_text=1, tile_rows=R, whole_tiles=nq)
+            == ws_size(c, s, n_splits=1, n_splits_text=1, tile_rows=R))
 
 
 def test_tile_rows_option():
@@ -281,23 +303,28 @@ def test_automatic_split_only_for_small_grids():
     assert any(ok)
 
 
-def test_automatic_two_splits_fill_the_last_round():
+def test_automatic_split_fills_the_last_round():
     """Without a device (256 compute units assumed): a 16-head grid whose last
-    round of blocks is half empty and whose query tiles visit >= 16,384 keys
-    (the 1280x704 steady state: 26,400 queries, 18-frame ring) is split in
-    two; the same grid with short key lists (the 480x832 segment), and the
-    2-head share (one round of blocks), are not.  The automatic workspace size
-    must equal the one of the forced split count."""
+    round of blocks is partly empty and whose query tiles visit long key
+    lists (the 1280x704 steady state: 26,400 queries, 18-frame ring) keeps
+    its leading tiles whole for the full rounds and splits the last tiles of
+    every head so that their pieces fill the last round; the same grid with
+    short key lists (the 480x832 segment), and the 2-head share (one round of
+    blocks), are not split.  The automatic workspace size must equal the one
+    of the forced choice."""
 
-    def ws(H, P, frames, W_, splits=0):
+    def ws(H, P, frames, W_, splits=0, whole=0):
         c = fake_cache(H=H, P=P, W=W_)
         c.frames_seen = W_          # a full ring of history
         c.segments = 0
         seg = hn.SegLayout(0, frames, P, 16, [], [], [])
-        return ws_size(c, seg, n_splits=splits, n_splits_text=1)
+        return ws_size(c, seg, n_splits=splits, n_splits_text=1, whole_tiles=whole)
 
-    steady = (16, 880, 30, 18)       # 1,104 blocks of 384 rows: 4.3 rounds
-    assert ws(*steady) == ws(*steady, splits=2) != ws(*steady, splits=1)
+    # 1,104 blocks of 384 rows: 4 full rounds and 80 blocks; the last 5 tiles
+    # of each head are split three ways (240 pieces for the last round)
+    steady = (16, 880, 30, 18)
+    assert ws(*steady) == ws(*steady, splits=3, whole=64) != ws(*steady, splits=2)
+    assert ws(*steady, splits=2) != ws(*steady, splits=1)
     short = (16, 390, 30, 1)         # 12,106 keys per query tile
     assert ws(*short) == ws(*short, splits=1)
     share = (2, 880, 30, 18)         # 208 blocks: one round either way
@@ -307,10 +334,11 @@ def test_automatic_two_splits_fill_the_last_round():
 def test_text_split_count_follows_the_round_model():
     """Without a device (256 compute units assumed): the text tiles of a joint
     launch are split so that they fill what the video blocks leave free.  The
-    480x832 segment (736 unsplit video blocks: 32 slots free in the last
-    round) takes 4; the 1280x704 steady state (video split in two: 13 full
-    rounds) takes 8; short text tiles stay whole.  The automatic workspace
-    size must equal the one of the forced count."""
+    480x832 segment (496 unsplit video blocks of 384 rows: 16 slots free in
+    the last round) takes 4; so does the 1280x704 steady state (4 full
+    rounds of whole video blocks, then 240 split pieces); short text tiles
+    stay whole.  The automatic workspace size must equal the one of the
+    forced count."""
 
     def ws(H, P, frames, W_, text_splits=0, head=768, tails=(128,) * 4):
         c = fake_cache(H=H, P=P, W=W_, cap=4096)
@@ -322,7 +350,7 @@ def test_text_split_count_follows_the_round_model():
     first = (16, 390, 30, 1)
     assert ws(*first) == ws(*first, text_splits=4) != ws(*first, text_splits=8)
     steady = (16, 880, 30, 18)
-    assert ws(*steady) == ws(*steady, text_splits=8) != ws(*steady, text_splits=4)
+    assert ws(*steady) == ws(*steady, text_splits=4) != ws(*steady, text_splits=8)
     short = (2, 24, 2, 4)
     assert ws(*short, head=16, tails=(8, 8)) == ws(*short, text_splits=1, head=16, tails=(8, 8))
 

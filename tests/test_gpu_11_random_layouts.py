@@ -4,7 +4,8 @@ Each case draws a segment sequence (1-4 segments of 1-5 latent frames, 1-97
 tokens per frame, heads of 0-40 tokens, 0-3 action tails with random
 windows, some empty), a history window (or none), 1-4 attention heads,
 normal or heavy-tailed keys and values, sometimes a keep list, and the plan
-options (tile height, forced key splits for video and text tiles).  The
+options (tile height, forced key splits for video and text tiles, leading
+video tiles left whole).  The
 cache is filled through hn_kv_quant_append and the query segment's video
 and text queries attend in one call; every row of both outputs and of the
 LSE is compared with the oracle at the bar; the DENSE expansion of the plan
@@ -52,8 +53,12 @@ def _layout(seed):
                    sparse_seed=(900 + seed) if keep else None)
     # a keep list fixes 128-row query tiles
     rows = int(rng.choice([0, 128] if keep else [0, 128, 256, 384]))
-    opts = hn.PlanOpts(n_splits=int(rng.choice([0, 1, 2, 3])), n_splits_text=int(rng.choice([0, 1, 2])),
-                       tile_rows=rows)
+    n_splits = int(rng.choice([0, 1, 2, 3]))
+    n_splits_text = int(rng.choice([0, 1, 2]))
+    # with a forced split, sometimes the leading video tiles whole (>= the
+    # tile count: no split)
+    whole = int(rng.integers(0, 3)) if n_splits > 1 else 0
+    opts = hn.PlanOpts(n_splits=n_splits, n_splits_text=n_splits_text, tile_rows=rows, whole_tiles=whole)
     return w, opts
 
 
@@ -63,7 +68,8 @@ def test_random_layout(seed):
     cur = w.current
     print(f"[random] seed {seed}: H={w.heads} S={w.query_segment} W={w.window} "
           f"segments={[(s.frames, s.tokens_per_frame, s.head_len, s.action_len, s.action_f0, s.action_f1) for s in w.segments]} "
-          f"{w.kv_dist} keep={w.sparse_keep} opts=({opts.n_splits},{opts.n_splits_text},{opts.tile_rows})",
+          f"{w.kv_dist} keep={w.sparse_keep} opts=({opts.n_splits},{opts.n_splits_text},{opts.tile_rows},"
+          f"{opts.whole_tiles})",
           flush=True)
     d = W.generate(w)
     run = G.Run(w, d, opts=opts)

@@ -4,7 +4,8 @@ partial results merged; one softmax over the union of keys).
 The split count is forced through the plan options on layouts with masks,
 ragged tiles, history, keep lists and text queries, and on the head-share
 layout c3_h2 (2 heads of the 1280x704 steady state); more splits than 64-key
-blocks leave some splits empty.  (The automatic choice is host logic, tested
+blocks leave some splits empty.  Hybrid plans (the leading video query
+tiles whole, the others split) are forced the same way.  (The automatic choice is host logic, tested
 in test_abi_host.py.)
 Bar: the same as without splits, against the fp64 oracle.
 """
@@ -61,6 +62,49 @@ def test_forced_splits(name, splits, text_splits):
     # and the video-only call (text tiles planned but not launched) agrees bit for bit
     assert torch.equal(run.attn()[0], o)
     assert torch.equal(o, o2)
+
+
+@pytest.mark.parametrize("name,rows,splits,whole,text_splits", [
+    ("m1", 128, 2, 1, 1), ("m2", 128, 3, 2, 2), ("m2", 128, 2, 4, 1), ("m2", 256, 5, 1, 3),
+    ("m2", 384, 3, 1, 1), ("m3", 128, 2, 1, 1), ("m3", 128, 3, 2, 2), ("m4", 128, 4, 2, 3)])
+def test_hybrid_splits(name, rows, splits, whole, text_splits):
+    """The first `whole` video query tiles run unsplit, the others split:
+    whole tiles write their outputs directly, split ones partials that the
+    merge combines; dispatched whole tiles first on every XCD."""
+    print(f"[split] {name} rows={rows} x{splits} whole={whole} text x{text_splits}", flush=True)
+    w = W.config(name)
+    d = data_of(name)
+    run = G.Run(w, d, opts=hn.PlanOpts(n_splits=splits, n_splits_text=text_splits, tile_rows=rows,
+                                       whole_tiles=whole))
+    assert run.plan.c.n_splits == splits and run.plan.c.n_whole == whole
+    assert run.plan.c.n_qtiles > whole
+    o, o_txt, lse, lse_txt = run.attn_joint()
+    ref_t, ref_lse_t, _ = oracle.attention(w, d, np.arange(w.current.text_len), queries="text")
+    _bar(w, o_txt.float().cpu().numpy(), ref_t)
+    assert np.abs(lse_txt.cpu().numpy() - ref_lse_t).max() <= 1e-2
+    ref, ref_lse, _ = oracle.attention(w, d, np.arange(w.current.video_len))
+    err = _bar(w, o.float().cpu().numpy(), ref)
+    print(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
+    assert np.abs(lse.cpu().numpy() - ref_lse).max() <= 1e-2
+    o_only, lse_only = run.attn()
+    assert torch.equal(o_only.view(torch.int16), o.view(torch.int16)) and torch.equal(lse_only, lse)
+    o2 = run.attn_joint()[0]
+    assert torch.equal(o2.view(torch.int16), o.view(torch.int16))
+
+
+def test_head_share_hybrid_split():
+    # c3_h2 with its first 90 of 104 query tiles whole and the last 14 split in 3
+    print("[split] c3_h2 x3 whole=90", flush=True)
+    w = W.config("c3_h2")
+    d = data_of("c3_h2")
+    run = G.Run(w, d, opts=hn.PlanOpts(n_splits=3, tile_rows=256, whole_tiles=90))
+    assert run.plan.c.n_splits == 3 and run.plan.c.n_whole == 90
+    o, lse = run.attn()
+    rows = G.sample_rows(w.current.video_len)
+    ref, ref_lse, _ = oracle.attention(w, d, rows)
+    err = _bar(w, o.float().cpu().numpy()[rows], ref)
+    print(f"  max-abs {err.max():.3e} mean-abs {err.mean():.3e}", flush=True)
+    assert np.abs(lse.cpu().numpy()[:, rows] - ref_lse).max() <= 1e-2
 
 
 def test_head_share_forced_split():
