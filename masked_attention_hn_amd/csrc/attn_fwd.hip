@@ -150,22 +150,15 @@ struct TileDesc {
   bool ok16;
 };
 
-// Maximum of two scores as gfx950's v_maximum3_f32 takes it (M3; a NaN
-// wins, as it would in any case through the exponentials): unlike fmaxf it
-// needs no quieting of the MFMA results first, two instructions fewer per 16
-// scores.  (The 384-row INT8 instance keeps fmaxf: with v_maximum3 its
-// register allocation spills.)
-template <bool M3 = true>
-__device__ inline float smax(float a, float b) {
-  if constexpr (M3) return __builtin_elementwise_maximum(a, b);
-  else return fmaxf(a, b);
-}
+// Maximum of two scores as gfx950's v_maximum3_f32 takes it (a NaN wins, as
+// it would in any case through the exponentials): unlike fmaxf it needs no
+// quieting of the MFMA results first, two instructions fewer per 16 scores.
+__device__ inline float smax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
 
 // max / sum of a value and its lane^32 partner
-template <bool M3 = false>
 __device__ inline float pair_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return smax<M3>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return smax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ inline float pair_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -529,16 +522,16 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
             float v = s[q][kb][4 * r + i] * scale[q];
             if (kb * 32 + 8 * r + i >= nkg) v = -INFINITY;
             s[q][kb][4 * r + i] = v;
-            mx = smax<!TIGHT>(mx, v);
+            mx = smax(mx, v);
           }
       } else {
         float m0 = s[q][kb][0];
 #pragma unroll
-        for (int i = 1; i < 16; ++i) m0 = smax<!TIGHT>(m0, s[q][kb][i]);
-        mx = smax<!TIGHT>(mx, m0 * scale[q]);
+        for (int i = 1; i < 16; ++i) m0 = smax(m0, s[q][kb][i]);
+        mx = smax(mx, m0 * scale[q]);
       }
     }
-    mx = pair_max<!TIGHT>(mx);
+    mx = pair_max(mx);
     if (__any(mx > st[q].m + RESCALE_SLACK)) {
       const float m_new = fmaxf(st[q].m, mx);
       const float alpha = (m_new == -INFINITY) ? 1.0f : __builtin_amdgcn_exp2f(st[q].m - m_new);
