@@ -96,6 +96,34 @@ def counter_traffic(workload):
     return round((fetch + write) * 1024)
 
 
+def max_engine_clock_mhz():
+    """Highest engine clock level the amdgpu driver lists for an AMD card
+    (sysfs pp_dpm_sclk), or None where it cannot be read."""
+    import glob
+    import re
+    best = None
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(os.path.join(os.path.dirname(f), "vendor")) as fh:
+                if fh.read().strip() != "0x1002":
+                    continue
+            with open(f) as fh:
+                mhz = [int(m) for m in re.findall(r"(\d+)\s*[Mm]hz", fh.read())]
+        except OSError:
+            continue
+        if mhz:
+            best = max(mhz) if best is None else max(best, max(mhz))
+    return best
+
+
+def device_info():
+    """The GPU the line was measured on, and what its bf16 peak assumes."""
+    props = torch.cuda.get_device_properties(0)
+    return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count, "max_engine_clock_mhz": max_engine_clock_mhz(),
+            "peak_basis": "published MI355X dense bf16 MFMA 2.5 PFLOP/s (256 CUs at 2.4 GHz); HBM 8 TB/s"}
+
+
 def visible_pairs_text(w):
     """Unmasked (text query, key) pairs per head, from the layout (no oracle):
     every text row sees earlier heads, kept history video, its own head and
@@ -460,6 +488,7 @@ def main():
             "visible_pairs_per_head": pairs,
         },
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "device": device_info(),
         "roofline": {
             "kernel": "seg_attn_fwd_kernel",
             "bound": "mfma",
