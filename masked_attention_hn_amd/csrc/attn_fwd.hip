@@ -7,14 +7,17 @@
 // bf16 for the segment's own keys and values, fp16 for the dequantized
 // history (see "tile" below).
 //
-// Work decomposition (template <NW, QB, KT>)
+// Work decomposition (template <NW, QB, KT, QL, SW>)
 //   block  = one (head, query tile of 32*QB*NW rows); NW waves, each owning
 //            QB blocks of 32 query rows.  Every K/V operand a wave reads from
 //            LDS feeds QB MFMAs; QB = 2 would halve the LDS traffic per flop
 //            but needs more than 256 VGPRs (one wave per SIMD), which measured
-//            slower, so the instances below use QB = 1: 8 waves x 32 rows, one
-//            block per CU, for dense plans; 4 waves x 32 rows, two blocks per
-//            CU, for keep-list plans (the keep list's 128-row query tile).
+//            slower, so the instances below use QB = 1: for dense plans 8
+//            waves x 32 rows (Q in registers) or 12 waves x 32 rows (three
+//            per SIMD; Q in LDS, QL, and the first SW = 8 waves staging), one
+//            block per CU, whichever the plan chose; 4 waves x 32 rows, two
+//            blocks per CU, for keep-list plans (the keep list's 128-row
+//            query tile).
 //   tile   = KT keys of one span of the tile plan, staged in LDS as bf16 in
 //            operand-major order, so that every MFMA operand a wave reads is
 //            64 consecutive slots (conflict-free); the V^T operand of the PV
@@ -54,7 +57,8 @@
 //            loads of tile n+1 are in flight while tile n is computed.
 //   grid   = XCD-aware: block b runs on XCD b % 8, and each XCD gets a
 //            contiguous range of (head, tile) tasks, so one head's keys and
-//            values stay in one XCD's L2.
+//            values stay in one XCD's L2; with a hybrid key split, the whole
+//            query tiles first and then the split pieces, on every XCD.
 #include <climits>
 #include <type_traits>
 
