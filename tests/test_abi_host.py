@@ -164,6 +164,16 @@ def test_attention_rejects_stale_plan():
     plan.n_splits_text = 17
     assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
     plan.n_splits_text = 1
+    # leading whole tiles only with a split, and fewer than the query tiles
+    plan.n_whole = 1               # without a split
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.n_splits = 2
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER        # 1 whole of 1 query tile
+    plan.n_whole = -1
+    assert call(s, ctypes.byref(plan)) == hn.HN_ERR_ORDER
+    plan.n_whole = 0
+    assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID   # a valid split plan
+    plan.n_splits = 1
     assert call(s, None) == hn.HN_ERR_NULL
     assert call(s, ctypes.byref(plan), scale=float("nan")) == hn.HN_ERR_INVALID
     assert call(s, ctypes.byref(plan), scale=-0.1) == hn.HN_ERR_INVALID   # positive scales only
