@@ -118,6 +118,7 @@ def max_engine_clock_mhz():
 
 def device_info():
     """The GPU the line was measured on, and what its bf16 peak assumes."""
+    import torch
     props = torch.cuda.get_device_properties(0)
     return {"name": props.name, "arch": getattr(props, "gcnArchName", None),
             "compute_units": props.multi_processor_count, "max_engine_clock_mhz": max_engine_clock_mhz(),

@@ -47,3 +47,35 @@ def test_multi_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_device_info_fields(monkeypatch):
+    """device_info() runs on its own (bench imports torch inside main) and
+    reports name, architecture and compute units of device 0."""
+    import torch
+
+    class Props:
+        name = "AMD Instinct MI355X"
+        gcnArchName = "gfx950:sramecc+:xnack-"
+        multi_processor_count = 256
+
+    monkeypatch.setattr(torch.cuda, "get_device_properties", lambda i: Props())
+    d = bench.device_info()
+    assert d["name"] == Props.name and d["arch"] == Props.gcnArchName and d["compute_units"] == 256
+    assert "max_engine_clock_mhz" in d and "2.4 GHz" in d["peak_basis"]
+
+
+def test_engine_clock_from_sysfs_levels(tmp_path, monkeypatch):
+    """The highest level of an AMD card's pp_dpm_sclk; other vendors ignored."""
+    import glob as _glob
+    amd = tmp_path / "card1" / "device"
+    amd.mkdir(parents=True)
+    (amd / "vendor").write_text("0x1002\n")
+    (amd / "pp_dpm_sclk").write_text("0: 500Mhz\n1: 1800Mhz *\n2: 2400Mhz\n")
+    other = tmp_path / "card0" / "device"
+    other.mkdir(parents=True)
+    (other / "vendor").write_text("0x1a03\n")
+    (other / "pp_dpm_sclk").write_text("0: 9999Mhz\n")
+    real = _glob.glob
+    monkeypatch.setattr(_glob, "glob", lambda pat: sorted(real(str(tmp_path / "card*" / "device" / "pp_dpm_sclk"))))
+    assert bench.max_engine_clock_mhz() == 2400
