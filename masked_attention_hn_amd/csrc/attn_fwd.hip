@@ -75,10 +75,10 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 #ifndef HN_QL_KLOOK
-#define HN_QL_KLOOK 5
+#define HN_QL_KLOOK 4
 #endif
 #ifndef HN_QL_VLOOK
-#define HN_QL_VLOOK 4
+#define HN_QL_VLOOK 3
 #endif
 #ifndef HN_QL_QLOOK
 #define HN_QL_QLOOK 2
