@@ -74,6 +74,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
+#ifndef HN_KLOOK
+#define HN_KLOOK 5
+#endif
+#ifndef HN_VLOOK
+#define HN_VLOOK 4
+#endif
 #ifndef HN_QL_KLOOK
 #define HN_QL_KLOOK 4
 #endif
@@ -480,7 +486,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   // to itself the compiler reads one or two ahead and waits on LDS): +2% on
   // the 480x832 segment and on the 1280x704 steady state.
   {
-    constexpr int NK = 8 * KB, KLOOK = TIGHT ? HN_QLI_KLOOK : (C::QL ? HN_QL_KLOOK : 5),
+    constexpr int NK = 8 * KB, KLOOK = TIGHT ? HN_QLI_KLOOK : (C::QL ? HN_QL_KLOOK : HN_KLOOK),
                   QLOOK = TIGHT ? HN_QLI_QLOOK : HN_QL_QLOOK;
     bf16x8 kk[NK];
     bf16x8 qq[8];
@@ -596,7 +602,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   // itself the compiler reads one or two operands ahead and waits on LDS
   // before the MFMA): +0.4-1.8% on the 480x832 segment and the 1280x704
   // history, same-run.
-  constexpr int NP = 8 * KB, VLOOK = TIGHT ? HN_QLI_VLOOK : (C::QL ? HN_QL_VLOOK : 4);
+  constexpr int NP = 8 * KB, VLOOK = TIGHT ? HN_QLI_VLOOK : (C::QL ? HN_QL_VLOOK : HN_VLOOK);
   auto vaddr = [&](int i) __attribute__((always_inline)) {
     const int kb = i / 8, t = (i / 4) % 2, c = i % 4;
     return vl + ((c * KB + kb) * 2 + t) * 512;
