@@ -90,10 +90,10 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #define HN_QL_QLOOK 2
 #endif
 #ifndef HN_QLI_KLOOK
-#define HN_QLI_KLOOK 3
+#define HN_QLI_KLOOK 4
 #endif
 #ifndef HN_QLI_VLOOK
-#define HN_QLI_VLOOK 3
+#define HN_QLI_VLOOK 2
 #endif
 #ifndef HN_QLI_QLOOK
 #define HN_QLI_QLOOK 2
