@@ -463,8 +463,9 @@ struct RowState {
 // O = acc / l.  scale[q] is the score scale (log2 units) of query block q.
 // With Q in LDS (QL) the QK loop reads the wave's Q chunks from qw (the
 // lane's slot of chunk 0), QLOOK chunks ahead, instead of qreg.  TIGHT: the
-// kernel also carries INT8 staging registers, and the operand lookaheads are
-// shortened to fit its 168 VGPRs without spilling.
+// kernel also carries INT8 staging registers in its 168 VGPRs, and takes the
+// operand lookaheads that measured fastest there (a few registers spill,
+// outside the MFMA loops).
 template <class C, bool MASK, bool QK16, bool PV16, bool TIGHT = false>
 __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qreg)[C::QB][8], const __bf16* qw,
                                           f32x16 (&acc)[C::QB][4], RowState (&st)[C::QB],
