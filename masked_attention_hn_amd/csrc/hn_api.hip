@@ -702,15 +702,17 @@ hn_status hn_kv_quant_append(hn_kv_cache* c, const hn_seg_layout* s, const void*
   std::memset(&p, 0, sizeof(p));
   p.H = c->num_heads;
   p.head_len = s->head_len;
-  p.vid_frame0 = s->frames - surv;
-  p.vid_first = p.vid_frame0 * P;
+  const int frame0 = s->frames - surv;  // first surviving frame of the segment
+  p.vid_first = frame0 * P;
   p.n_vid = surv * P;
   p.P = P;
   p.W = c->window_frames;
-  p.frames_seen = c->frames_seen;
+  p.slot0 = (int32_t)((c->frames_seen + frame0) % c->window_frames);
   p.head_pos = c->head_tokens;
   p.head_cap = c->head_cap_tokens;
   p.ring_cap = c->window_frames * P;
+  hn::div_magic((uint32_t)p.H, p.mag_h, p.sh_h);
+  hn::div_magic((uint32_t)P, p.mag_p, p.sh_p);
   p.k_txt = static_cast<const __bf16*>(k_txt);
   p.v_txt = static_cast<const __bf16*>(v_txt);
   p.k_vid = static_cast<const __bf16*>(k_vid);

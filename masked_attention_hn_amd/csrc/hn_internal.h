@@ -186,6 +186,18 @@ struct MergeParams {
   float* lse_txt;
 };
 
+// Multiplier m and shift k for unsigned division by d >= 1 of numerators
+// below 2^31: with l = ceil(log2 d), k = 31 + l and m = ceil(2^k / d) (at
+// most 2^32 - 1), n / d == (n * m) >> k for every n < 2^31, because
+// 0 <= m d - 2^k < d <= 2^l = 2^(k - 31) (Granlund and Montgomery, "Division
+// by invariant integers using multiplication", PLDI 1994, section 4).
+inline void div_magic(uint32_t d, uint32_t& m, int32_t& k) {
+  int l = 0;
+  while ((1ull << l) < d) ++l;
+  k = 31 + l;
+  m = (uint32_t)(((1ull << k) + d - 1) / d);
+}
+
 struct AppendParams {
   int32_t H;
   int32_t head_len;       // head rows to store
@@ -193,11 +205,12 @@ struct AppendParams {
   int32_t n_vid;          // surviving video rows
   int32_t P;
   int32_t W;
-  int64_t frames_seen;    // before this append
+  int32_t slot0;          // ring slot of the first surviving frame
   int32_t head_pos;       // head-store row of the first new head token
   int32_t head_cap;
   int32_t ring_cap;       // W*P
-  int32_t vid_frame0;     // local frame of vid_first
+  uint32_t mag_h, mag_p;  // division by H and by P: n / H == (n * mag_h) >> sh_h
+  int32_t sh_h, sh_p;     //   for n < 2^31 (div_magic)
   const __bf16* k_txt;
   const __bf16* v_txt;
   const __bf16* k_vid;
