@@ -433,7 +433,8 @@ hn_status hn_seg_attn_fwd_noalloc(const hn_kv_cache* cache, const hn_seg_layout*
  * k_cam, v_cam : bf16 [F][H][D] (device), one token per latent frame
  * o_vid        : bf16 [F*P][H][D] (output; must not alias the inputs)
  * lse          : fp32 [H][F*P] natural-log softmax normaliser, or NULL
- * Errors: HN_ERR_NULL, HN_ERR_INVALID (shape, radius < 0, non-finite scale).
+ * Errors: HN_ERR_NULL, HN_ERR_INVALID (shape, radius < 0, non-finite scale),
+ * HN_ERR_UNSUPPORTED (F*P*H of 2^28 (token, head) rows or more).
  */
 hn_status hn_camera_attn_fwd(const hn_seg_layout* seg, int32_t num_heads, int32_t radius,
                              const void* q_vid, const void* k_cam, const void* v_cam,

@@ -889,8 +889,11 @@ hn_status hn_camera_attn_fwd(const hn_seg_layout* s, int32_t num_heads, int32_t 
   if (!q_vid || !k_cam || !v_cam || !o_vid) return fail(HN_ERR_NULL, "q/k/v/o pointer is NULL");
   if (!std::isfinite(sm_scale)) return fail(HN_ERR_INVALID, "sm_scale is not finite");
   const int64_t rows = (int64_t)s->frames * s->tokens_per_frame;
-  if (rows * num_heads > ((int64_t)1 << 40))
-    return fail(HN_ERR_UNSUPPORTED, "segment of %lld tokens x %d heads too large", (long long)rows, num_heads);
+  // (token, head) row numbers stay below 2^28, and with 16 rows per
+  // 256-thread block the launch's thread count below 2^32
+  if (rows * num_heads >= ((int64_t)1 << 28) || (rows + 15) / 16 * num_heads >= ((int64_t)1 << 24))
+    return fail(HN_ERR_UNSUPPORTED, "segment of %lld tokens x %d heads: 2^28 rows or more", (long long)rows,
+                num_heads);
   hn::CameraParams p;
   std::memset(&p, 0, sizeof(p));
   p.H = num_heads;
@@ -899,6 +902,8 @@ hn_status hn_camera_attn_fwd(const hn_seg_layout* s, int32_t num_heads, int32_t 
   p.radius = std::min(radius, s->frames);
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.rows = rows;
+  hn::div_magic((uint32_t)p.H, p.mag_h, p.sh_h);
+  hn::div_magic((uint32_t)p.P, p.mag_p, p.sh_p);
   p.q = static_cast<const __bf16*>(q_vid);
   p.k = static_cast<const __bf16*>(k_cam);
   p.v = static_cast<const __bf16*>(v_cam);

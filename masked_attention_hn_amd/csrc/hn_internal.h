@@ -242,8 +242,9 @@ struct CameraParams {
   int32_t F;             // latent frames (= camera tokens)
   int32_t radius;        // visible camera tokens: |f' - f| <= radius
   float scale_log2;      // sm_scale * log2(e)
-  int32_t pad0;
-  int64_t rows;          // F * P video tokens
+  int32_t sh_h, sh_p;    // division by H and by P (div_magic): n / H == (n * mag_h) >> sh_h
+  uint32_t mag_h, mag_p;
+  int64_t rows;          // F * P video tokens (< 2^28 / H, so every index below 2^31)
   const __bf16* q;       // [rows][H][D]
   const __bf16* k;       // [F][H][D]
   const __bf16* v;       // [F][H][D]

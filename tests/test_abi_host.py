@@ -412,6 +412,11 @@ def test_camera_checks():
     assert cam(ctypes.byref(s.c), 2, -1, *args, 0.1, None) == hn.HN_ERR_INVALID
     assert cam(ctypes.byref(s.c), 2, 0, *args, float("inf"), None) == hn.HN_ERR_INVALID
     assert cam(ctypes.byref(s.c), 2, 0, FAKE, None, FAKE, FAKE, None, 0.1, None) == hn.HN_ERR_NULL
+    # (token, head) rows are numbered in 28 bits: 1,024 frames x 16,384 tokens
+    # x 16 heads = 2^28 rows is refused before any launch
+    big = hn.SegLayout(0, 1024, 16384, 0, [], [], [])
+    assert cam(ctypes.byref(big.c), 16, 0, *args, 0.1, None) == hn.HN_ERR_UNSUPPORTED
+    assert "2^28" in hn.hn_last_error()
 
 
 def test_attention_rejects_sources_over_2gib():
