@@ -362,6 +362,30 @@ def main():
         del kv_big
     append_big["shape"] = "1280x704 segment, no window: (768 + 30 x 880) tokens x 16 heads"
 
+    def time_copy(nbytes):
+        """A plain device copy (torch) moving the same bytes (half read, half
+        written), rotating buffers over > 600 MB, launches back to back: what
+        HBM delivers to a copy of this size, the reference for the append."""
+        half = nbytes // 2
+        n_sets = max(3, math.ceil(600e6 / nbytes))
+        src = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        for a, b in zip(src, dst):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        reps = 4 * n_sets
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for i in range(reps):
+            dst[i % n_sets].copy_(src[i % n_sets])
+        c1.record(stream)
+        torch.cuda.synchronize()
+        ms = c0.elapsed_time(c1) / reps
+        return {"bytes": 2 * half, "ms_per_launch": round(ms, 4),
+                "achieved": round(2 * half / (ms * 1e-3) / 1e9, 1), "unit": "GB/s"}
+
+    append_big["plain_copy_same_bytes"] = time_copy(append_big["bytes"])
+
     traffic = counter_traffic(args.workload)
 
     # camera cross-attention: each video token attends to the camera tokens of
