@@ -89,6 +89,13 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #ifndef HN_QL_QLOOK
 #define HN_QL_QLOOK 2
 #endif
+// QL, bf16-only instance: the first QRES 16-d chunks of the wave's Q stay in
+// registers and only the rest are read from LDS every tile (2 of 8 chunks:
+// 8 more VGPRs, 166 of the 168 three waves per SIMD allow; c2 1.0667 ->
+// 1.0612 ms, same run; 3 chunks spill)
+#ifndef HN_QL_QRES
+#define HN_QL_QRES 2
+#endif
 #ifndef HN_QLI_KLOOK
 #define HN_QLI_KLOOK 4
 #endif
@@ -462,7 +469,8 @@ struct RowState {
 // the 16-bit probabilities the PV MFMA consumes, so their rounding cancels in
 // O = acc / l.  scale[q] is the score scale (log2 units) of query block q.
 // With Q in LDS (QL) the QK loop reads the wave's Q chunks from qw (the
-// lane's slot of chunk 0), QLOOK chunks ahead, instead of qreg.  TIGHT: the
+// lane's slot of chunk 0), QLOOK chunks ahead, instead of qreg, except the
+// first QRES chunks, which stay in qreg (bf16-only instance).  TIGHT: the
 // kernel also carries INT8 staging registers in its 168 VGPRs, and takes the
 // operand lookaheads that measured fastest there (a few registers spill,
 // outside the MFMA loops).
@@ -488,12 +496,12 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
   // the 480x832 segment and on the 1280x704 steady state.
   {
     constexpr int NK = 8 * KB, KLOOK = TIGHT ? HN_QLI_KLOOK : (C::QL ? HN_QL_KLOOK : HN_KLOOK),
-                  QLOOK = TIGHT ? HN_QLI_QLOOK : HN_QL_QLOOK;
+                  QLOOK = TIGHT ? HN_QLI_QLOOK : HN_QL_QLOOK, QRES = (TIGHT || !C::QL) ? 0 : HN_QL_QRES;
     bf16x8 kk[NK];
     bf16x8 qq[8];
     if constexpr (C::QL) {
 #pragma unroll
-      for (int t = 0; t < QLOOK; ++t) qq[t] = ld8(qw + t * 512);
+      for (int t = QRES; t < QRES + QLOOK && t < 8; ++t) qq[t] = ld8(qw + t * 512);
     }
 #pragma unroll
     for (int i = 0; i < KLOOK; ++i) kk[i] = ld8(kl + ((i % KB) * 8 + i / KB) * 512);
@@ -502,7 +510,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
       const int t = i / KB, kb = i % KB;
 #pragma unroll
       for (int q = 0; q < QB; ++q) {
-        const bf16x8 qop = C::QL ? qq[t] : qreg[q][t];
+        const bf16x8 qop = C::QL ? (t < QRES ? qreg[0][t] : qq[t]) : qreg[q][t];
         if constexpr (QK16)
           s[q][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, kk[i]),
                                                             __builtin_bit_cast(f16x8, qop), s[q][kb], 0, 0, 0);
@@ -511,7 +519,7 @@ __device__ __forceinline__ void tile_math(const Stage<C>& sb, const bf16x8 (&qre
       }
       if (i + KLOOK < NK) kk[i + KLOOK] = ld8(kl + (((i + KLOOK) % KB) * 8 + (i + KLOOK) / KB) * 512);
       if constexpr (C::QL) {
-        if (kb == KB - 1 && t + QLOOK < 8) qq[t + QLOOK] = ld8(qw + (t + QLOOK) * 512);
+        if (kb == KB - 1 && t >= QRES && t + QLOOK < 8) qq[t + QLOOK] = ld8(qw + (t + QLOOK) * 512);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
