@@ -80,21 +80,28 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 #ifndef HN_VLOOK
 #define HN_VLOOK 4
 #endif
+// QL, bf16-only instance (384-row blocks on the segment's own keys): the
+// first QRES 16-d chunks of the wave's Q stay in registers and only the rest
+// are read from LDS every tile, the others QLOOK chunks ahead; K and V
+// operands are read KLOOK / VLOOK MFMAs ahead.  With 166 of the 168 VGPRs
+// three waves per SIMD allow, resident Q chunks trade against operand
+// lookahead; on the 480x832 segment (ms per launch, two passes each, same
+// run) QRES/KLOOK/VLOOK/QLOOK 0/4/3/2 1.0667, 2/4/3/2 1.0612; on another
+// box 2/4/3/2 1.0484, 4/2/3/2 1.0437, 4/2/2/2 1.0433, 5/2/2/1 1.0420,
+// 5/2/3/1 1.0429, 4/3/2/1 1.0439, 4/3/3/1 1.0452, 5/1/3/2 1.0567,
+// 6/1/2/2 1.0537 (one K operand ahead is too few); combinations that spill
+// were not run.
 #ifndef HN_QL_KLOOK
-#define HN_QL_KLOOK 4
+#define HN_QL_KLOOK 2
 #endif
 #ifndef HN_QL_VLOOK
-#define HN_QL_VLOOK 3
+#define HN_QL_VLOOK 2
 #endif
 #ifndef HN_QL_QLOOK
-#define HN_QL_QLOOK 2
+#define HN_QL_QLOOK 1
 #endif
-// QL, bf16-only instance: the first QRES 16-d chunks of the wave's Q stay in
-// registers and only the rest are read from LDS every tile (2 of 8 chunks:
-// 8 more VGPRs, 166 of the 168 three waves per SIMD allow; c2 1.0667 ->
-// 1.0612 ms, same run; 3 chunks spill)
 #ifndef HN_QL_QRES
-#define HN_QL_QRES 2
+#define HN_QL_QRES 5
 #endif
 #ifndef HN_QLI_KLOOK
 #define HN_QLI_KLOOK 4
