@@ -14,8 +14,9 @@
 //            but needs more than 256 VGPRs (one wave per SIMD), which measured
 //            slower, so the instances below use QB = 1: for dense plans 8
 //            waves x 32 rows (Q in registers) or 12 waves x 32 rows (three
-//            per SIMD; Q in LDS, QL, and the first SW = 8 waves staging), one
-//            block per CU, whichever the plan chose; 4 waves x 32 rows, two
+//            per SIMD; Q in LDS, QL, and the first SW = 8 waves staging; the
+//            bf16-only instance keeps five of a wave's eight Q chunks in
+//            registers as well), one block per CU, whichever the plan chose; 4 waves x 32 rows, two
 //            blocks per CU, for keep-list plans (the keep list's 128-row
 //            query tile).
 //   tile   = KT keys of one span of the tile plan, staged in LDS as bf16 in
